@@ -1,0 +1,260 @@
+"""Pins of the oracle's per-token NVFP4 quantize/dequantize.
+
+Passages ("Towards Blackwell-native 8-bit and 4-bit RL"):
+* section "Format background": E2M1 values, one E4M3 scale per 16 values rounded to the
+  nearest representable value, plus a coarse FP32 scale whose scope is a recipe choice;
+* section "Per-token activation scaling": one FP32 scale per token, computed online; a
+  token's quantized bytes must not depend on the other tokens of the batch; gate and up
+  projections are quantized together;
+* section "High-precision and dequantized backward": BF16 dequantized operands.
+And the NVIDIA NVFP4 pretraining note (Russian page): at least 6.25% of each block
+(the block-amax element, 1 of 16) is represented at close to FP8 precision.
+"""
+from fractions import Fraction
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from oracle import exact
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, *v = line.split()
+            out[k] = v
+    return out
+
+
+def _bf16_exact(vals) -> np.ndarray:
+    f = np.array([float(v) for v in vals], dtype=np.float32)
+    b = workloads.bf16_bits_from_f32(f)
+    assert np.array_equal(workloads.f32_from_bf16_bits(b), f)
+    # keep the sign of negative zero written as "-0"
+    b[np.signbit(f)] |= np.uint16(0x8000)
+    return b
+
+
+def _unpack(q):
+    lo = q & np.uint8(0xF)
+    hi = q >> np.uint8(4)
+    return np.stack([lo, hi], axis=-1).reshape(q.shape[0], -1)
+
+
+# --------------------------------------------------------------------------- handmade
+
+def test_handmade_row_matches_golden():
+    g = _read_golden("nvfp4_handmade.txt")
+    x = _bf16_exact(g["x"])[None, :]
+    q, sb, st = oracle.nv_quantize_per_token(x)
+    assert [int(c, 16) for c in g["codes"]] == list(_unpack(q)[0])
+    assert [int(c, 16) for c in g["q"]] == list(q[0])
+    assert [int(c, 16) for c in g["sb"]] == list(sb[0])
+    assert st[0] == float(g["st"][0])
+    y = oracle.nv_dequantize(q, sb, st)
+    assert np.array_equal(y[0], _bf16_exact(g["y"]))
+
+
+# --------------------------------------------------------------------------- exact checker
+
+def _rows_of_every_kind(rng, n, K):
+    """Rows of the kinds the pages name for quantizer tests: random, boundary, zeros,
+    maxes; plus BF16-subnormal rows and rows with one huge outlier."""
+    rows = []
+    for i in range(n):
+        kind = i % 7
+        if kind == 0:
+            v = rng.standard_normal(K) * np.exp2(rng.integers(-126, 120))
+            rows.append(workloads.bf16_bits_from_f32(v.astype(np.float32)))
+        elif kind == 1:
+            b = rng.integers(0, 1 << 16, K).astype(np.uint16)
+            b[(b & 0x7F80) == 0x7F80] &= np.uint16(0xBFFF)
+            rows.append(b)
+        elif kind == 2:
+            b = np.zeros(K, np.uint16)
+            b[rng.random(K) < 0.5] = 0x8000
+            if rng.random() < 0.5:
+                b[rng.integers(K)] = 0x3F80      # one lone 1.0 in a zero row
+            rows.append(b)
+        elif kind == 3:                          # maxes: 2688*2^k and BF16 max
+            k = int(rng.integers(-130, 115))
+            v = np.full(K, 2688.0 * 2.0 ** k, np.float32)
+            b = workloads.bf16_bits_from_f32(v)
+            if rng.random() < 0.3:
+                b[rng.integers(K)] = 0x7F7F
+            b[rng.random(K) < 0.5] |= np.uint16(0x8000)
+            rows.append(b)
+        elif kind == 4:                          # boundary: E2M1 midpoints x block step
+            v = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 4.0], K) * np.exp2(rng.integers(-20, 20))
+            v *= np.where(rng.random(K) < 0.5, -1, 1)
+            rows.append(workloads.bf16_bits_from_f32(v.astype(np.float32)))
+        elif kind == 5:                          # BF16 subnormal row (tiny s_t)
+            b = rng.integers(0, 0x100, K).astype(np.uint16)
+            b[rng.random(K) < 0.5] |= np.uint16(0x8000)
+            rows.append(b)
+        else:                                    # one outlier: many blocks' scales underflow
+            v = rng.standard_normal(K) * 1e-3
+            v[rng.integers(K)] = 3e4
+            rows.append(workloads.bf16_bits_from_f32(v.astype(np.float32)))
+    return np.stack(rows)
+
+
+def test_nv_oracle_matches_exact_checker_on_tiny_rows():
+    rng = np.random.default_rng(31)
+    x = _rows_of_every_kind(rng, 140, 32)
+    q, sb, st = oracle.nv_quantize_per_token(x)
+    for r in range(x.shape[0]):
+        packed, sbs, s_t = exact.nv_row([int(v) for v in x[r]])
+        assert list(sb[r]) == sbs, r
+        assert list(q[r]) == packed, r
+        assert Fraction(float(st[r])) == s_t, r
+
+
+def test_nv_dequant_every_code_and_scale_matches_exact():
+    rng = np.random.default_rng(32)
+    sts = [1.0, 2.0 ** -140, 3.1e-5, 7.7e30, 0.0, float(np.float32(1 / 3))]
+    sts += list(np.float32(rng.standard_normal(4) * 10.0 ** rng.integers(-30, 30, 4)).astype(float))
+    for s_t in sts:
+        s_t = float(np.float32(abs(s_t)))
+        # one row: 16 codes per block x 256 block scales (K = 4096)
+        codes = np.tile(np.arange(16, dtype=np.uint8), 256)
+        q = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)[None, :]
+        sb = np.arange(256, dtype=np.uint8)[None, :]
+        y = oracle.nv_dequantize(q, sb, np.array([s_t], np.float32))
+        _, st_exact = exact.binary32_value(int(np.float32(s_t).view(np.uint32)))
+        for j in range(4096):
+            assert y[0, j] == exact.nv_dequant_one(int(codes[j]), j // 16, 0, st_exact), (s_t, j)
+
+
+# --------------------------------------------------------------------------- invariants
+
+def _block_amax(x, width):
+    a = np.abs(workloads.f32_from_bf16_bits(x).astype(np.float64))
+    return a.reshape(x.shape[0], -1, width).max(axis=2)
+
+
+def test_block_amax_element_is_six_when_block_scale_is_normal():
+    """The block-amax element lands on E2M1 6 (code 7) whenever DEC(sb) >= 2^-6: the
+    '6.25% of values near FP8 precision' property."""
+    x = workloads.config3(seed=33, tokens=256, materialize=False)["h"]
+    q, sb, st = oracle.nv_quantize_per_token(x)
+    codes = _unpack(q)
+    xa = np.abs(workloads.f32_from_bf16_bits(x)).reshape(x.shape[0], -1, 16)
+    arg = xa.argmax(axis=2)
+    c = np.take_along_axis(codes.reshape(x.shape[0], -1, 16), arg[..., None], axis=2)[..., 0]
+    dec = np.vectorize(oracle.dec_e4m3)(sb)
+    normal = dec >= 2.0 ** -6
+    assert normal.mean() > 0.9
+    assert np.all((c[normal] & 7) == 7)
+
+
+def test_block_holding_token_amax_gets_scale_448():
+    x = workloads.config3(seed=34, tokens=256, materialize=False)["h"]
+    q, sb, st = oracle.nv_quantize_per_token(x)
+    amax_b = _block_amax(x, 16)
+    hold = amax_b == amax_b.max(axis=1, keepdims=True)
+    assert np.all(sb[hold] == 0x7E)
+    assert np.all(sb[~hold] <= 0x7E)
+
+
+def test_per_token_invariance():
+    """A token's bytes do not depend on the rest of the batch: change, permute, split or
+    duplicate the other rows and every row's (q, sb, s_t) stays identical."""
+    rng = np.random.default_rng(35)
+    x = workloads.config3(seed=35, tokens=64, materialize=False)["h"]
+    q, sb, st = oracle.nv_quantize_per_token(x)
+    perm = rng.permutation(x.shape[0])
+    qp, sbp, stp = oracle.nv_quantize_per_token(x[perm])
+    assert np.array_equal(qp, q[perm]) and np.array_equal(sbp, sb[perm]) and np.array_equal(stp, st[perm])
+    y = x.copy()
+    y[1::2] = workloads.bf16_bits_from_f32(rng.standard_normal((32, x.shape[1])).astype(np.float32) * 1e4)
+    qy, sby, sty = oracle.nv_quantize_per_token(y)
+    assert np.array_equal(qy[0::2], q[0::2]) and np.array_equal(sty[0::2], st[0::2])
+    qa, sba, sta = oracle.nv_quantize_per_token(x[:17])
+    assert np.array_equal(qa, q[:17]) and np.array_equal(sba, sb[:17])
+    dup = np.repeat(x[:8], 8, axis=0)
+    qd, sbd, std = oracle.nv_quantize_per_token(dup)
+    assert np.array_equal(qd, np.repeat(q[:8], 8, axis=0))
+
+
+def test_gate_up_joint_equals_separate_under_per_row_scales():
+    e = workloads.config4_expert(0, ffn=64, hidden=128)
+    gu = e["gate_up"]
+    q, sb, st = oracle.nv_quantize_per_token(gu)
+    qg, sbg, stg = oracle.nv_quantize_per_token(gu[:64])
+    qu, sbu, stu = oracle.nv_quantize_per_token(gu[64:])
+    assert np.array_equal(q, np.concatenate([qg, qu])) and np.array_equal(st, np.concatenate([stg, stu]))
+
+
+def test_power_of_two_equivariance():
+    rng = np.random.default_rng(36)
+    x = workloads.bf16_bits_from_f32((rng.standard_normal((32, 256)) * 5).astype(np.float32))
+    q0, sb0, st0 = oracle.nv_quantize_per_token(x)
+    for k in (-30, -4, 3, 60):
+        xk = workloads.bf16_bits_from_f32(workloads.f32_from_bf16_bits(x) * np.float32(2.0 ** k))
+        qk, sbk, stk = oracle.nv_quantize_per_token(xk)
+        assert np.array_equal(qk, q0) and np.array_equal(sbk, sb0)
+        assert np.array_equal(stk, st0 * np.float32(2.0 ** k))
+
+
+def test_sign_symmetry():
+    x = workloads.config3(seed=37, tokens=32, materialize=False)["h"]
+    q, sb, st = oracle.nv_quantize_per_token(x)
+    qn, sbn, stn = oracle.nv_quantize_per_token(x ^ np.uint16(0x8000))
+    assert np.array_equal(sbn, sb) and np.array_equal(stn, st)
+    assert np.array_equal(qn, q ^ np.uint8(0x88))
+
+
+def test_zero_row_and_zero_block():
+    x = np.zeros((2, 64), np.uint16)
+    x[1, :16] = 0x8000
+    x[1, 16:32] = workloads.bf16_bits_from_f32(np.full(16, 3.0, np.float32))
+    q, sb, st = oracle.nv_quantize_per_token(x)
+    assert st[0] == 0.0 and np.all(sb[0] == 0) and np.all(q[0] == 0)
+    assert np.all(_unpack(q)[1, :16] == 8)            # negative zeros keep their sign
+    assert sb[1, 1] == 0x7E and np.all(sb[1, 2:] == 0)
+
+
+def test_error_bound_exact():
+    """|q*DEC(sb)*s_t - x| <= half the local E2M1 step * D * (1 + 2^-20), or the element
+    saturated at 6 (checked in exact arithmetic on normal-range rows)."""
+    x = workloads.config3(seed=38, tokens=24, materialize=False)["h"][:, :256]
+    q, sb, st = oracle.nv_quantize_per_token(x)
+    codes = _unpack(q)
+    grid = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4), Fraction(6)]
+    for r in range(x.shape[0]):
+        s_t = Fraction(float(st[r]))
+        for k in range(x.shape[1]):
+            c = int(codes[r, k])
+            d = exact.e4m3_value(int(sb[r, k // 16])) * s_t
+            _, xv = exact.bf16_value(int(x[r, k]))
+            qv = grid[c & 7] * d
+            step = grid[min((c & 7) + 1, 7)] - grid[c & 7] if (c & 7) < 7 else grid[7] - grid[6]
+            assert abs(qv - xv) <= step / 2 * d * (1 + Fraction(1, 1 << 20)) or (c & 7) == 7, (r, k)
+
+
+def test_grouped_is_flat_and_checks_offsets():
+    cfg = workloads.config3(seed=39, tokens=40)
+    x, off = cfg["x"], cfg["offsets"]
+    q, sb, st, ok = oracle.nv_quantize_per_token_grouped(x, off)
+    qf, sbf, stf = oracle.nv_quantize_per_token(x)
+    assert ok and np.array_equal(q, qf) and np.array_equal(sb, sbf) and np.array_equal(st, stf)
+    bad = off.copy()
+    bad[3], bad[4] = bad[4] + 1, bad[3]
+    assert not oracle.nv_quantize_per_token_grouped(x, bad)[3]
+    short = off.copy()
+    short[-1] = x.shape[0] - 1
+    assert not oracle.nv_quantize_per_token_grouped(x, short)[3]
+    first = off.copy()
+    first[0] = 1
+    assert not oracle.nv_quantize_per_token_grouped(x, first)[3]
