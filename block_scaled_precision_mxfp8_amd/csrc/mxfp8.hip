@@ -1,0 +1,312 @@
+// mxfp8.hip -- MXFP8 quantization (rowwise 1x32, columnwise 32x1, both) and MXFP8
+// dequantization to BF16 for gfx950.
+//
+// Page "Towards Blackwell-native 8-bit and 4-bit RL":
+//  * section "Format background": 32 consecutive E4M3 values share one E8M0 scale; the
+//    blocks are one-dimensional; the decoded scale is rounded up so the block maximum is
+//    never clipped.
+//  * section "Recipe 1: end-to-end MXFP8 RL": rowwise (1x32) and columnwise (32x1) blocks
+//    are numerically different, so both copies are quantized from the full-precision
+//    input, not one from the other.
+//  * section "High-precision and dequantized backward": BF16 dequantized operands.
+//
+// The work is pure streaming (about 3-4 bytes of HBM traffic per element and a few
+// integer/FP32 operations), so the kernels are written for HBM bandwidth: 16-byte loads
+// and stores that cover whole cache lines per instruction, block maxima reduced inside a
+// quad of lanes with DPP, and no LDS traffic on the element data.
+#include "bsq_device.h"
+
+namespace bsq {
+
+// ----------------------------------------------------------------------------- encode
+
+// Two E4M3 codes (bits 0-7 and 8-15) of the BF16 pair w scaled by inv = 2^-e.  The
+// product is exact and at most 448 (the scale never clips), so no saturation is needed.
+__device__ __forceinline__ uint32_t mx_enc2(uint32_t w, float inv) {
+    float lo = fabsf(__uint_as_float(bf16_lo_bits(w))) * inv;
+    float hi = fabsf(__uint_as_float(bf16_hi_bits(w))) * inv;
+    uint32_t c0 = e4m3_code(lo) | ((w >> 8) & 0x80u);
+    uint32_t c1 = e4m3_code(hi) | ((w >> 24) & 0x80u);
+    return c0 | (c1 << 8);
+}
+
+// Four E4M3 codes of two BF16 pairs, little-endian in one dword.
+__device__ __forceinline__ uint32_t mx_enc4(uint32_t w0, uint32_t w1, float inv) {
+    return mx_enc2(w0, inv) | (mx_enc2(w1, inv) << 16);
+}
+
+// Magnitude maximum (BF16 bits) of the 8 BF16 values of a 16-byte chunk.
+__device__ __forceinline__ uint32_t chunk_absmax(const uint4& v) {
+    uint32_t m = absmax2(absmax2(absmax2(absmax2(0u, v.x), v.y), v.z), v.w);
+    return fold2(m);
+}
+
+// ----------------------------------------------------------------------------- rowwise
+
+// Rowwise blocks of 32 never straddle a row (K % 32 == 0), and the row-major E4M3 and
+// E8M0 arrays are exactly the element and block orders of the flattened tensor, so the
+// rowwise copy is a 1-D stream over M*K elements.  One wave handles a tile of
+// ROW_SLOTS x 512 elements: in slot j lane l owns the 16-byte chunk (8 BF16) number
+// tile*64*ROW_SLOTS + 64*j + l, so each load instruction covers 1 KiB contiguous and each
+// quad of lanes holds one block.  The 16*ROW_SLOTS scale bytes of the tile are gathered
+// in LDS and written as 16-byte stores (one full 128-byte line for ROW_SLOTS = 8).
+constexpr int ROW_SLOTS = 8;
+constexpr int ROW_WAVES = 4;
+
+__global__ __launch_bounds__(64 * ROW_WAVES)
+void mx_quant_rowwise_kernel(const uint4* __restrict__ x, uint2* __restrict__ q,
+                             uint8_t* __restrict__ s, int64_t n_chunks) {
+    __shared__ __align__(16) uint8_t lds_s[ROW_WAVES][16 * ROW_SLOTS];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t base = ((int64_t)blockIdx.x * ROW_WAVES + wave) * (64 * ROW_SLOTS);
+    if (base >= n_chunks) return;
+
+    uint4 v[ROW_SLOTS];
+#pragma unroll
+    for (int j = 0; j < ROW_SLOTS; ++j) {
+        const int64_t c = base + 64 * j + lane;
+        v[j] = (c < n_chunks) ? x[c] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < ROW_SLOTS; ++j) {
+        const uint32_t amax = quad_max(chunk_absmax(v[j]));
+        const uint32_t code = e8m0_code_from_bf16_mag(amax);
+        const float inv = e8m0_inverse(code);
+        uint2 out;
+        out.x = mx_enc4(v[j].x, v[j].y, inv);
+        out.y = mx_enc4(v[j].z, v[j].w, inv);
+        const int64_t c = base + 64 * j + lane;
+        if (c < n_chunks) q[c] = out;
+        if ((lane & 3) == 0) lds_s[wave][16 * j + (lane >> 2)] = (uint8_t)code;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    const int64_t nblk = n_chunks >> 2;
+    const int64_t b0 = base >> 2;
+    if (b0 + 16 * ROW_SLOTS <= nblk) {
+        if (lane < ROW_SLOTS)
+            reinterpret_cast<uint4*>(s + b0)[lane] = reinterpret_cast<const uint4*>(lds_s[wave])[lane];
+    } else {
+        for (int i = lane; i < 16 * ROW_SLOTS; i += 64)
+            if (b0 + i < nblk) s[b0 + i] = lds_s[wave][i];
+    }
+}
+
+// ----------------------------------------------------------------------------- col / both
+
+// Columnwise (and dual) quantization of x[M][K].  One wave owns a 128-row x 64-column
+// tile.  Lane l = 8*g + c holds rows 16*g .. 16*g+15 of the tile and columns 8*c .. 8*c+7
+// (one 16-byte chunk per row, 16 chunks = 64 VGPRs):
+//  * a 32x1 column block is held by the lane pair (g, g^1) -- 16 rows each -- so its
+//    maximum is a lane-local packed max plus one lane exchange;
+//  * a 1x32 row block is the quad of lanes c = 4k .. 4k+3 of one row (DPP);
+//  * every load instruction reads 8 rows x 128 bytes (full lines);
+//  * the columnwise copy q_col[K][M] is written as one 16-byte store per lane and
+//    column (16 rows of E4M3), so 8 lanes g = 0..7 fill 128 contiguous bytes of one
+//    q_col row: the transpose happens in registers and the writes stay coalesced.
+// Four waves of a workgroup take four neighbouring 64-column tiles of the same 128 rows,
+// so the rowwise q/s lines they share are completed inside one CU's L2.  Workgroups are
+// renumbered so that each XCD (workgroups are dealt round-robin over the 8 XCDs) gets a
+// contiguous range of row stripes.
+constexpr int TILE_ROWS = 128;
+constexpr int TILE_COLS = 64;
+constexpr int TILE_WAVES = 4;
+
+template <bool ROW>
+__global__ __launch_bounds__(64 * TILE_WAVES) __attribute__((amdgpu_waves_per_eu(4)))
+void mx_quant_tile_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                          uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
+                          uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
+                          int64_t col_groups, int64_t n_wg) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 3;
+    const int c = lane & 7;
+
+    int64_t w = blockIdx.x;
+    if ((n_wg & 7) == 0) w = (w & 7) * (n_wg >> 3) + (w >> 3);   // XCD-contiguous ranges
+    const int64_t r0 = (w / col_groups) * TILE_ROWS;
+    const int64_t k0 = ((w % col_groups) * TILE_WAVES + wave) * TILE_COLS;
+    if (k0 >= K) return;
+
+    const int64_t row0 = r0 + 16 * g;          // first of this lane's 16 rows
+    const int64_t col0 = k0 + 8 * c;           // first of this lane's 8 columns
+    const bool rows_ok = row0 < M;             // M % 32 == 0: lane pairs agree
+    const bool cols_ok = col0 < K;             // K % 32 == 0: quads agree
+    const bool ok = rows_ok && cols_ok;
+
+    uint4 v[16];
+    const uint16_t* src = x + row0 * K + col0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        v[i] = ok ? *reinterpret_cast<const uint4*>(src + (int64_t)i * K) : make_uint4(0u, 0u, 0u, 0u);
+
+    // ---- rowwise copy: each row of the lane, block = quad of lanes
+    if (ROW) {
+        const int64_t nb_row = K >> 5;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t amax = quad_max(chunk_absmax(v[i]));
+            const uint32_t code = e8m0_code_from_bf16_mag(amax);
+            const float inv = e8m0_inverse(code);
+            uint2 out;
+            out.x = mx_enc4(v[i].x, v[i].y, inv);
+            out.y = mx_enc4(v[i].z, v[i].w, inv);
+            if (ok) {
+                *reinterpret_cast<uint2*>(q_row + (row0 + i) * K + col0) = out;
+                if ((c & 3) == 0) s_row[(row0 + i) * nb_row + (col0 >> 5)] = (uint8_t)code;
+            }
+        }
+        // The column pass below re-derives its FP32 operands from the packed tile; this
+        // empty register barrier stops the compiler from instead keeping the row pass's
+        // unpacked values alive (which would double the live tile and spill).
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
+    }
+
+    // ---- columnwise copy: packed column maxima over 16 rows, then over the lane pair
+    uint32_t cm[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        cm[0] = absmax2(cm[0], v[i].x);
+        cm[1] = absmax2(cm[1], v[i].y);
+        cm[2] = absmax2(cm[2], v[i].z);
+        cm[3] = absmax2(cm[3], v[i].w);
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t other = (uint32_t)__shfl_xor((int)cm[d], 8, 64);
+        u16x2 a = __builtin_bit_cast(u16x2, cm[d]);
+        u16x2 b = __builtin_bit_cast(u16x2, other);
+        cm[d] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+    }
+    const int64_t nb_col = M >> 5;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t code0 = e8m0_code_from_bf16_mag(cm[d] & 0xFFFFu);   // column 2d
+        const uint32_t code1 = e8m0_code_from_bf16_mag(cm[d] >> 16);       // column 2d+1
+        const float inv0 = e8m0_inverse(code0);
+        const float inv1 = e8m0_inverse(code1);
+        uint32_t a[4], b[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            uint32_t pa = 0u, pb = 0u;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t wv = (d == 0) ? v[4 * t + u].x : (d == 1) ? v[4 * t + u].y
+                                  : (d == 2) ? v[4 * t + u].z : v[4 * t + u].w;
+                const float lo = fabsf(__uint_as_float(bf16_lo_bits(wv))) * inv0;
+                const float hi = fabsf(__uint_as_float(bf16_hi_bits(wv))) * inv1;
+                pa |= (e4m3_code(lo) | ((wv >> 8) & 0x80u)) << (8 * u);
+                pb |= (e4m3_code(hi) | ((wv >> 24) & 0x80u)) << (8 * u);
+            }
+            a[t] = pa;
+            b[t] = pb;
+        }
+        if (ok) {
+            const int64_t ka = col0 + 2 * d;
+            *reinterpret_cast<uint4*>(q_col + ka * M + row0) = make_uint4(a[0], a[1], a[2], a[3]);
+            *reinterpret_cast<uint4*>(q_col + (ka + 1) * M + row0) = make_uint4(b[0], b[1], b[2], b[3]);
+            if ((g & 1) == 0) {
+                s_col[ka * nb_col + (row0 >> 5)] = (uint8_t)code0;
+                s_col[(ka + 1) * nb_col + (row0 >> 5)] = (uint8_t)code1;
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------- dequant
+
+// MXFP8 -> BF16 in the stored layout, again a 1-D stream: element i uses scale i/32.
+// Lane l of slot j owns the 16 codes of chunk tile*64*DQ_SLOTS + 64*j + l (half a block)
+// and writes 32 bytes of BF16.
+constexpr int DQ_SLOTS = 4;
+constexpr int DQ_WAVES = 4;
+
+__device__ __forceinline__ uint32_t mx_dec1(uint32_t code, float scale, bool nan_scale) {
+    const uint32_t mag = code & 0x7Fu;
+    const float v = e4m3_decode_mag(mag) * scale;                // exact, may be +inf
+    const uint32_t u = rne_bf16(__float_as_uint(v)) | ((code & 0x80u) << 8);
+    return (mag == 0x7Fu || nan_scale) ? 0x7FC0u : u;
+}
+
+__device__ __forceinline__ uint4 mx_dec8(uint32_t w0, uint32_t w1, float scale, bool nan_scale) {
+    uint4 o;
+    o.x = mx_dec1(w0 & 0xFF, scale, nan_scale) | (mx_dec1((w0 >> 8) & 0xFF, scale, nan_scale) << 16);
+    o.y = mx_dec1((w0 >> 16) & 0xFF, scale, nan_scale) | (mx_dec1(w0 >> 24, scale, nan_scale) << 16);
+    o.z = mx_dec1(w1 & 0xFF, scale, nan_scale) | (mx_dec1((w1 >> 8) & 0xFF, scale, nan_scale) << 16);
+    o.w = mx_dec1((w1 >> 16) & 0xFF, scale, nan_scale) | (mx_dec1(w1 >> 24, scale, nan_scale) << 16);
+    return o;
+}
+
+__global__ __launch_bounds__(64 * DQ_WAVES)
+void mx_dequant_kernel(const uint4* __restrict__ q, const uint8_t* __restrict__ s,
+                       uint4* __restrict__ y, int64_t n_chunks) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t base = ((int64_t)blockIdx.x * DQ_WAVES + wave) * (64 * DQ_SLOTS);
+    if (base >= n_chunks) return;
+    uint4 w[DQ_SLOTS];
+    uint32_t sc[DQ_SLOTS];
+#pragma unroll
+    for (int j = 0; j < DQ_SLOTS; ++j) {
+        const int64_t c = base + 64 * j + lane;
+        const bool ok = c < n_chunks;
+        w[j] = ok ? q[c] : make_uint4(0u, 0u, 0u, 0u);
+        sc[j] = ok ? s[c >> 1] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < DQ_SLOTS; ++j) {
+        const int64_t c = base + 64 * j + lane;
+        const float scale = e8m0_decode(sc[j]);
+        const bool nan_scale = sc[j] == 255u;
+        if (c < n_chunks) {
+            y[2 * c] = mx_dec8(w[j].x, w[j].y, scale, nan_scale);
+            y[2 * c + 1] = mx_dec8(w[j].z, w[j].w, scale, nan_scale);
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------- launch
+
+hipError_t launch_mx_quant(const void* x, int64_t M, int64_t K, int mode,
+                           void* q_row, void* s_row, void* q_col, void* s_col,
+                           hipStream_t stream) {
+    if (mode == 1) {
+        const int64_t n_chunks = M * K / 8;
+        const int64_t tiles = (n_chunks + 64 * ROW_SLOTS - 1) / (64 * ROW_SLOTS);
+        const int64_t grid = (tiles + ROW_WAVES - 1) / ROW_WAVES;
+        hipLaunchKernelGGL(mx_quant_rowwise_kernel, dim3((unsigned)grid), dim3(64 * ROW_WAVES), 0,
+                           stream, (const uint4*)x, (uint2*)q_row, (uint8_t*)s_row, n_chunks);
+        return hipGetLastError();
+    }
+    const int64_t row_stripes = (M + TILE_ROWS - 1) / TILE_ROWS;
+    const int64_t col_groups = (K + TILE_COLS * TILE_WAVES - 1) / (TILE_COLS * TILE_WAVES);
+    const int64_t n_wg = row_stripes * col_groups;
+    if (mode == 3) {
+        hipLaunchKernelGGL(mx_quant_tile_kernel<true>, dim3((unsigned)n_wg), dim3(64 * TILE_WAVES), 0,
+                           stream, (const uint16_t*)x, M, K, (uint8_t*)q_row, (uint8_t*)s_row,
+                           (uint8_t*)q_col, (uint8_t*)s_col, col_groups, n_wg);
+    } else {
+        hipLaunchKernelGGL(mx_quant_tile_kernel<false>, dim3((unsigned)n_wg), dim3(64 * TILE_WAVES), 0,
+                           stream, (const uint16_t*)x, M, K, (uint8_t*)nullptr, (uint8_t*)nullptr,
+                           (uint8_t*)q_col, (uint8_t*)s_col, col_groups, n_wg);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_dequant(const void* q, const void* s, int64_t rows, int64_t cols,
+                             void* y, hipStream_t stream) {
+    const int64_t n_chunks = rows * cols / 16;
+    const int64_t tiles = (n_chunks + 64 * DQ_SLOTS - 1) / (64 * DQ_SLOTS);
+    const int64_t grid = (tiles + DQ_WAVES - 1) / DQ_WAVES;
+    hipLaunchKernelGGL(mx_dequant_kernel, dim3((unsigned)grid), dim3(64 * DQ_WAVES), 0, stream,
+                       (const uint4*)q, (const uint8_t*)s, (uint4*)y, n_chunks);
+    return hipGetLastError();
+}
+
+}  // namespace bsq

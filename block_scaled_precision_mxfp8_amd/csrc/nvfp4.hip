@@ -1,0 +1,270 @@
+// nvfp4.hip -- per-token NVFP4 quantization (flat and grouped by expert) and NVFP4
+// dequantization to BF16 for gfx950.
+//
+// Page "Towards Blackwell-native 8-bit and 4-bit RL":
+//  * section "Format background": E2M1 values, one E4M3 scale per 16 values rounded to
+//    the nearest representable value, and a coarse FP32 scale that maps the tensor or
+//    token into the NVFP4 range; which range the FP32 scale covers is a recipe choice.
+//  * section "Per-token activation scaling": one FP32 activation scale per token,
+//    computed online, so that no token's bytes depend on other tokens of the batch; the
+//    single call that emits packed FP4 and the E4M3 block scales also returns the
+//    per-token FP32 scales (no separate calibration pass).
+//  * section "High-precision and dequantized backward": BF16 dequantized operands.
+//
+// The per-token scale needs the whole row before any element can be encoded.  A wave
+// owns a row and keeps it in registers (16-byte loads, 8 BF16 per lane per slot), so the
+// row is read from HBM exactly once: row maximum by a wave reduction, then each 1x16
+// block (a lane pair) is scaled and encoded from registers.
+#include <float.h>
+
+#include "bsq_device.h"
+
+namespace bsq {
+
+// Eight E2M1 codes (one nibble each, element 2j in the low nibble of byte j) of the
+// BF16 values of a 16-byte chunk multiplied by f: q = ENC_E2M1(fl(x * f)).  The sign of
+// fl(x * f) is the sign of x because f >= 0.
+__device__ __forceinline__ uint32_t nv_enc2(uint32_t w, float f) {
+    const float lo = fabsf(__uint_as_float(bf16_lo_bits(w))) * f;
+    const float hi = fabsf(__uint_as_float(bf16_hi_bits(w))) * f;
+    const uint32_t c0 = e2m1_code(lo) | ((w >> 12) & 0x8u);
+    const uint32_t c1 = e2m1_code(hi) | ((w >> 28) & 0x8u);
+    return c0 | (c1 << 4);
+}
+
+__device__ __forceinline__ uint32_t nv_enc8(const uint4& v, float f) {
+    return nv_enc2(v.x, f) | (nv_enc2(v.y, f) << 8) | (nv_enc2(v.z, f) << 16) | (nv_enc2(v.w, f) << 24);
+}
+
+__device__ __forceinline__ uint32_t chunk_absmax8(const uint4& v) {
+    return fold2(absmax2(absmax2(absmax2(absmax2(0u, v.x), v.y), v.z), v.w));
+}
+
+// Block scale code, and the element multiplier of the block, from the block maximum
+// (BF16 magnitude bits) and the token scale s_t:
+//   sb = ENC_E4M3(fl(amax_b / fl(6 s_t))) (0 if s_t == 0),  D = fl(DEC(sb) s_t),
+//   f = 0 if D == 0 else min(fl(1 / D), FLT_MAX).
+// Both divisions are IEEE binary32 divisions (correctly rounded, denormals kept).
+__device__ __forceinline__ uint32_t nv_block_scale(uint32_t amax_b_bits, float s_t, float p, float& f) {
+    const float amax_b = __uint_as_float(amax_b_bits << 16);
+    const uint32_t code = (s_t == 0.0f) ? 0u : e4m3_code(amax_b / p);
+    const float d = e4m3_decode_mag(code) * s_t;
+    f = (d == 0.0f) ? 0.0f : fminf(1.0f / d, FLT_MAX);
+    return code;
+}
+
+// Device-side check of the expert offsets of the grouped call, by one wave:
+// offsets[0] == 0, offsets[E] == R, offsets[e] <= offsets[e+1].
+__device__ void check_offsets(const int64_t* __restrict__ off, int64_t E, int64_t R,
+                              int32_t* __restrict__ status) {
+    const int lane = threadIdx.x & 63;
+    bool bad = false;
+    for (int64_t e = lane; e < E; e += 64) bad |= off[e] > off[e + 1];
+    if (lane == 0) bad |= (off[0] != 0) || (off[E] != R);
+    const bool any_bad = __any(bad);
+    if (lane == 0) *status = any_bad ? 6 /* BSQ_ERR_OFFSETS */ : 0;
+}
+
+__global__ __launch_bounds__(64)
+void nv_check_offsets_kernel(const int64_t* __restrict__ off, int64_t E, int64_t R,
+                             int32_t* __restrict__ status) {
+    check_offsets(off, E, R, status);
+}
+
+// One wave per row, the row held in registers: NS slots of 64 lanes x 8 BF16 (so rows of
+// up to 512*NS elements).  Lane l of slot j holds elements 512 j + 8 l .. +7; a 1x16
+// block is the lane pair (2i, 2i+1).
+constexpr int NV_WAVES = 4;
+
+template <int NS>
+__global__ __launch_bounds__(64 * NV_WAVES)
+void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
+                          uint8_t* __restrict__ sb, float* __restrict__ st,
+                          int64_t R, int64_t K,
+                          const int64_t* __restrict__ offsets, int64_t E,
+                          int32_t* __restrict__ status) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    if (status != nullptr && blockIdx.x == 0 && wave == 0) check_offsets(offsets, E, R, status);
+    const int64_t row = (int64_t)blockIdx.x * NV_WAVES + wave;
+    if (row >= R) return;
+
+    const int64_t cpr = K >> 3;                       // 8-element chunks per row
+    const uint4* xr = x + row * cpr;
+    uint4 v[NS];
+    uint32_t m = 0u;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const int64_t ch = 64 * j + lane;
+        v[j] = (ch < cpr) ? xr[ch] : make_uint4(0u, 0u, 0u, 0u);
+        m = max(m, chunk_absmax8(v[j]));
+    }
+    const uint32_t amax_t = group_max<64>(m);
+    const float s_t = __uint_as_float(amax_t << 16) / 2688.0f;     // fl(amax / (6 * 448))
+    const float p = 6.0f * s_t;                                     // fl(6 s_t)
+
+    uint32_t* qr = q + row * cpr;                     // 4 bytes of q per chunk
+    uint8_t* sbr = sb + row * (K >> 4);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const int64_t ch = 64 * j + lane;
+        const uint32_t amax_b = pair_max(chunk_absmax8(v[j]));
+        float f;
+        const uint32_t code = nv_block_scale(amax_b, s_t, p, f);
+        const uint32_t packed = nv_enc8(v[j], f);
+        if (ch < cpr) {
+            qr[ch] = packed;
+            if ((lane & 1) == 0) sbr[ch >> 1] = (uint8_t)code;
+        }
+    }
+    if (lane == 0) st[row] = s_t;
+}
+
+// Rows longer than the register-resident variants: two passes over the row (the second
+// read of a row is served by the caches), same arithmetic.
+__global__ __launch_bounds__(64 * NV_WAVES)
+void nv_quant_rows_long_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
+                               uint8_t* __restrict__ sb, float* __restrict__ st,
+                               int64_t R, int64_t K,
+                               const int64_t* __restrict__ offsets, int64_t E,
+                               int32_t* __restrict__ status) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    if (status != nullptr && blockIdx.x == 0 && wave == 0) check_offsets(offsets, E, R, status);
+    const int64_t row = (int64_t)blockIdx.x * NV_WAVES + wave;
+    if (row >= R) return;
+    const int64_t cpr = K >> 3;
+    const uint4* xr = x + row * cpr;
+    uint32_t m = 0u;
+    for (int64_t base = 0; base < cpr; base += 64) {
+        const int64_t ch = base + lane;
+        if (ch < cpr) m = max(m, chunk_absmax8(xr[ch]));
+    }
+    const uint32_t amax_t = group_max<64>(m);
+    const float s_t = __uint_as_float(amax_t << 16) / 2688.0f;
+    const float p = 6.0f * s_t;
+    uint32_t* qr = q + row * cpr;
+    uint8_t* sbr = sb + row * (K >> 4);
+    for (int64_t base = 0; base < cpr; base += 64) {
+        const int64_t ch = base + lane;
+        const uint4 v = (ch < cpr) ? xr[ch] : make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t amax_b = pair_max(chunk_absmax8(v));
+        float f;
+        const uint32_t code = nv_block_scale(amax_b, s_t, p, f);
+        const uint32_t packed = nv_enc8(v, f);
+        if (ch < cpr) {
+            qr[ch] = packed;
+            if ((lane & 1) == 0) sbr[ch >> 1] = (uint8_t)code;
+        }
+    }
+    if (lane == 0) st[row] = s_t;
+}
+
+// ----------------------------------------------------------------------------- dequant
+
+// NVFP4 -> BF16: lane l of slot j owns one 16-element block (8 bytes of q) and writes
+// 32 bytes of BF16.  y = RNE_BF16(fl(exact(DEC_E2M1(q) DEC_E4M3(sb)) s_t)).
+constexpr int NVDQ_SLOTS = 4;
+constexpr int NVDQ_WAVES = 4;
+
+__device__ __forceinline__ uint32_t nv_dec1(uint32_t nib, float bscale, float s_t) {
+    const float e = e2m1_decode_mag(nib & 7u);
+    const float inner = ((nib & 8u) ? -e : e) * bscale;      // exact (<= 6 significant bits)
+    const uint32_t u = __float_as_uint(inner * s_t);          // one binary32 rounding
+    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC0u : rne_bf16(u) & 0xFFFFu;
+}
+
+__global__ __launch_bounds__(64 * NVDQ_WAVES)
+void nv_dequant_kernel(const uint2* __restrict__ q, const uint8_t* __restrict__ sb,
+                       const float* __restrict__ st, uint4* __restrict__ y,
+                       int64_t n_blocks, int64_t blocks_per_row, double inv_bpr) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t base = ((int64_t)blockIdx.x * NVDQ_WAVES + wave) * (64 * NVDQ_SLOTS);
+    if (base >= n_blocks) return;
+    uint2 w[NVDQ_SLOTS];
+    uint32_t code[NVDQ_SLOTS];
+    float s_t[NVDQ_SLOTS];
+#pragma unroll
+    for (int j = 0; j < NVDQ_SLOTS; ++j) {
+        const int64_t b = base + 64 * j + lane;
+        const bool ok = b < n_blocks;
+        // row = b / blocks_per_row from a binary64 estimate, corrected by one step each way
+        int64_t r = (int64_t)((double)b * inv_bpr);
+        if ((r + 1) * blocks_per_row <= b) ++r;
+        if (r * blocks_per_row > b) --r;
+        w[j] = ok ? q[b] : make_uint2(0u, 0u);
+        code[j] = ok ? sb[b] : 0u;
+        s_t[j] = ok ? st[r] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < NVDQ_SLOTS; ++j) {
+        const int64_t b = base + 64 * j + lane;
+        const uint32_t mag = code[j] & 0x7Fu;
+        const float bm = e4m3_decode_mag(mag);
+        const float bscale = (mag == 0x7Fu) ? __uint_as_float(0x7FC00000u)
+                                            : ((code[j] & 0x80u) ? -bm : bm);
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t word = (i < 4) ? w[j].x : w[j].y;
+            const uint32_t byte = (word >> (8 * (i & 3))) & 0xFFu;
+            o[i] = nv_dec1(byte & 0xFu, bscale, s_t[j]) | (nv_dec1(byte >> 4, bscale, s_t[j]) << 16);
+        }
+        if (b < n_blocks) {
+            y[2 * b] = make_uint4(o[0], o[1], o[2], o[3]);
+            y[2 * b + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------- launch
+
+template <int NS>
+static void launch_rows(const void* x, int64_t R, int64_t K, void* q, void* sb, float* st,
+                        const int64_t* off, int64_t E, int32_t* status, hipStream_t stream) {
+    const int64_t grid = (R + NV_WAVES - 1) / NV_WAVES;
+    hipLaunchKernelGGL(nv_quant_rows_kernel<NS>, dim3((unsigned)grid), dim3(64 * NV_WAVES), 0, stream,
+                       (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, st, R, K, off, E, status);
+}
+
+hipError_t launch_nv_quant(const void* x, int64_t R, int64_t K, void* q, void* sb, float* st,
+                           const int64_t* offsets, int64_t E, int32_t* status,
+                           hipStream_t stream) {
+    const int64_t slots = (K / 8 + 63) / 64;
+    const int64_t grid = (R + NV_WAVES - 1) / NV_WAVES;
+    if (R == 0 || K == 0) {
+        // nothing to quantize; still report on the offsets when asked to
+        if (status != nullptr)
+            hipLaunchKernelGGL(nv_check_offsets_kernel, dim3(1), dim3(64), 0, stream, offsets, E, R,
+                               status);
+        return hipGetLastError();
+    }
+    switch (slots) {
+        case 1: launch_rows<1>(x, R, K, q, sb, st, offsets, E, status, stream); break;
+        case 2: launch_rows<2>(x, R, K, q, sb, st, offsets, E, status, stream); break;
+        case 3: launch_rows<3>(x, R, K, q, sb, st, offsets, E, status, stream); break;
+        case 4: launch_rows<4>(x, R, K, q, sb, st, offsets, E, status, stream); break;
+        case 5: case 6: launch_rows<6>(x, R, K, q, sb, st, offsets, E, status, stream); break;
+        case 7: case 8: launch_rows<8>(x, R, K, q, sb, st, offsets, E, status, stream); break;
+        default:
+            hipLaunchKernelGGL(nv_quant_rows_long_kernel, dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
+                               stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, st, R, K,
+                               offsets, E, status);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_nv_dequant(const void* q, const void* sb, const float* st, int64_t R, int64_t K,
+                             void* y, hipStream_t stream) {
+    const int64_t n_blocks = R * (K / 16);
+    const int64_t bpr = K / 16;
+    const int64_t tiles = (n_blocks + 64 * NVDQ_SLOTS - 1) / (64 * NVDQ_SLOTS);
+    const int64_t grid = (tiles + NVDQ_WAVES - 1) / NVDQ_WAVES;
+    hipLaunchKernelGGL(nv_dequant_kernel, dim3((unsigned)grid), dim3(64 * NVDQ_WAVES), 0, stream,
+                       (const uint2*)q, (const uint8_t*)sb, st, (uint4*)y, n_blocks, bpr,
+                       1.0 / (double)bpr);
+    return hipGetLastError();
+}
+
+}  // namespace bsq

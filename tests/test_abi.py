@@ -1,0 +1,168 @@
+"""The C ABI library loads without a GPU, exports every symbol include/bsq.h declares, and
+rejects bad arguments on the host before any HIP call.
+
+No call here reaches a kernel launch: every call is either invalid (caught by host
+validation) or has a zero size (a documented no-op that makes no HIP call), so fake
+pointers are safe.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_precision_mxfp8_amd as bsq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsq.h")
+
+A = 0x10000          # a 16-byte aligned fake device address
+B = 0x20000000
+C = 0x40000000
+D = 0x60000000
+E_ = 0x70000000
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bsq.LIB_PATH):
+        from block_scaled_precision_mxfp8_amd import build
+        build.build()
+    return bsq.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z_0-9]*\s*\*?\s*([A-Za-z_][A-Za-z_0-9]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = _declared_functions()
+    for n in ("mx_quantize_mxfp8", "nv_quantize_nvfp4_per_token",
+              "nv_quantize_nvfp4_per_token_grouped", "mx_dequantize", "nv_dequantize",
+              "bsq_status_string", "bsq_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in _declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert bsq.abi_version() == 1
+    for s in range(0, 8):
+        assert bsq.status_string(s) and bsq.status_string(s) != "unknown status"
+    assert bsq.status_string(99) == "unknown status"
+
+
+# ---------------------------------------------------------------------------------------
+# mx_quantize_mxfp8
+
+def mxq(L, x=A, M=64, K=64, mode=3, qr=B, sr=C, qc=D, sc=E_):
+    return L.mx_quantize_mxfp8(x, M, K, mode, qr, sr, qc, sc, None)
+
+
+def test_mx_quant_validation(L):
+    assert mxq(L, mode=0) == bsq.BSQ_ERR_MODE
+    assert mxq(L, mode=4) == bsq.BSQ_ERR_MODE
+    assert mxq(L, M=-1) == bsq.BSQ_ERR_SHAPE
+    assert mxq(L, K=-32) == bsq.BSQ_ERR_SHAPE
+    assert mxq(L, K=48) == bsq.BSQ_ERR_SHAPE                  # K % 32
+    assert mxq(L, M=48, mode=3) == bsq.BSQ_ERR_SHAPE          # M % 32 for the columnwise copy
+    assert mxq(L, M=48, mode=2) == bsq.BSQ_ERR_SHAPE
+    assert mxq(L, M=2 ** 40, K=2 ** 40) == bsq.BSQ_ERR_SHAPE  # size overflow
+    assert mxq(L, x=None) == bsq.BSQ_ERR_NULL
+    assert mxq(L, mode=1, sr=None) == bsq.BSQ_ERR_NULL
+    assert mxq(L, mode=2, qc=None) == bsq.BSQ_ERR_NULL
+    assert mxq(L, mode=3, sc=None) == bsq.BSQ_ERR_NULL
+    assert mxq(L, x=A + 8) == bsq.BSQ_ERR_ALIGN
+    assert mxq(L, qr=B + 4) == bsq.BSQ_ERR_ALIGN
+    assert mxq(L, sc=E_ + 1) == bsq.BSQ_ERR_ALIGN
+    assert mxq(L, qr=A + 16) == bsq.BSQ_ERR_ALIAS              # output inside the input
+    assert mxq(L, qc=B + 64 * 64 - 16) == bsq.BSQ_ERR_ALIAS    # two outputs overlap
+
+
+def test_mx_quant_zero_sizes_are_noops(L):
+    assert mxq(L, M=0) == bsq.BSQ_OK
+    assert mxq(L, K=0, x=None, qr=None) == bsq.BSQ_OK
+    assert mxq(L, M=0, mode=1, x=None, qr=None, sr=None) == bsq.BSQ_OK
+
+
+def test_mx_quant_unused_copy_pointers_are_ignored(L):
+    # rowwise only: the columnwise pointers may be anything, even misaligned
+    assert mxq(L, mode=1, qc=3, sc=5, M=0) == bsq.BSQ_OK
+    assert mxq(L, mode=1, qc=3, sc=5, K=48) == bsq.BSQ_ERR_SHAPE
+
+
+# ---------------------------------------------------------------------------------------
+# nv quantize (flat and grouped)
+
+def nvq(L, x=A, R=4, K=64, q=B, sb=C, st=D):
+    return L.nv_quantize_nvfp4_per_token(x, R, K, q, sb, st, None)
+
+
+def nvg(L, x=A, R=4, K=64, off=E_, E=2, q=B, sb=C, st=D, status=None):
+    return L.nv_quantize_nvfp4_per_token_grouped(x, R, K, off, E, q, sb, st, status, None)
+
+
+def test_nv_quant_validation(L):
+    assert nvq(L, K=24) == bsq.BSQ_ERR_SHAPE
+    assert nvq(L, R=-1) == bsq.BSQ_ERR_SHAPE
+    assert nvq(L, x=None) == bsq.BSQ_ERR_NULL
+    assert nvq(L, st=None) == bsq.BSQ_ERR_NULL
+    assert nvq(L, q=B + 2) == bsq.BSQ_ERR_ALIGN
+    assert nvq(L, st=D + 4) == bsq.BSQ_ERR_ALIGN
+    assert nvq(L, sb=B + 16) == bsq.BSQ_ERR_ALIAS
+    assert nvq(L, R=0) == bsq.BSQ_OK
+    assert nvq(L, K=0, x=None, q=None) == bsq.BSQ_OK
+
+
+def test_nv_grouped_validation(L):
+    assert nvg(L, E=0) == bsq.BSQ_ERR_SHAPE
+    assert nvg(L, E=-3) == bsq.BSQ_ERR_SHAPE
+    assert nvg(L, off=None) == bsq.BSQ_ERR_NULL
+    assert nvg(L, off=E_ + 4) == bsq.BSQ_ERR_ALIGN
+    assert nvg(L, status=E_ + 0x1002) == bsq.BSQ_ERR_ALIGN
+    assert nvg(L, off=A + 8) == bsq.BSQ_ERR_ALIAS             # offsets inside the input
+    assert nvg(L, status=B) == bsq.BSQ_ERR_ALIAS               # status inside q
+    assert nvg(L, K=40) == bsq.BSQ_ERR_SHAPE
+    assert nvg(L, R=0) == bsq.BSQ_OK                           # no status asked: nothing to do
+
+
+# ---------------------------------------------------------------------------------------
+# dequant
+
+def test_mx_dequant_validation(L):
+    f = L.mx_dequantize
+    assert f(A, B, 4, 48, C, None) == bsq.BSQ_ERR_SHAPE
+    assert f(A, B, -4, 64, C, None) == bsq.BSQ_ERR_SHAPE
+    assert f(None, B, 4, 64, C, None) == bsq.BSQ_ERR_NULL
+    assert f(A, B, 4, 64, None, None) == bsq.BSQ_ERR_NULL
+    assert f(A + 1, B, 4, 64, C, None) == bsq.BSQ_ERR_ALIGN
+    assert f(A, A + 16, 4, 64, C, None) == bsq.BSQ_ERR_ALIAS
+    assert f(A, B, 4, 64, B - 16, None) == bsq.BSQ_ERR_ALIAS   # y runs into the scales
+    assert f(A, B, 0, 64, C, None) == bsq.BSQ_OK
+
+
+def test_nv_dequant_validation(L):
+    f = L.nv_dequantize
+    assert f(A, B, C, 4, 40, D, None) == bsq.BSQ_ERR_SHAPE
+    assert f(A, B, None, 4, 64, D, None) == bsq.BSQ_ERR_NULL
+    assert f(A, B, C + 4, 4, 64, D, None) == bsq.BSQ_ERR_ALIGN
+    assert f(A, B, C, 4, 64, A + 16, None) == bsq.BSQ_ERR_ALIAS
+    assert f(A, B, C, 0, 64, D, None) == bsq.BSQ_OK
+
+
+def test_binding_refuses_cpu_tensors_without_calling_the_library():
+    import torch
+    x = torch.zeros(32, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        bsq.mx_quantize_mxfp8(x, "both")
+    with pytest.raises(ValueError):
+        bsq.nv_quantize_nvfp4_per_token(x)
+    with pytest.raises(ValueError):
+        bsq.mx_quantize_mxfp8(x, "bogus")

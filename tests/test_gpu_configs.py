@@ -1,0 +1,143 @@
+"""GPU parity at the full sizes of the five workloads (seeded synthetic inputs shaped like
+a Qwen3-30B-A3B-class MoE layer; recipes in workloads/__init__.py), with the same launch
+configuration the benchmark times.  Every output byte is compared with the CPU oracle,
+except the 524288 routed rows of the layer-step workload, which are compared on a
+seeded sample of rows (each row's NVFP4 bytes depend on that row only).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_mxfp8_amd as bsq
+import oracle
+import workloads
+from gpu_helpers import assert_same, bits, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_mx(name, x_np, xd, mode):
+    M, K = x_np.shape
+    q_row, s_row, q_col, s_col = bsq.mx_quantize_mxfp8(xd, mode)
+    if q_row is not None:
+        eq, es = oracle.mx_quantize_rowwise(x_np)
+        assert_same(name + " q_row", bits(q_row), eq)
+        assert_same(name + " s_row", bits(s_row), es)
+        assert_same(name + " dequant row", bits(bsq.mx_dequantize(q_row, s_row)),
+                    oracle.mx_dequantize(eq, es))
+    if q_col is not None:
+        eq, es = oracle.mx_quantize_colwise(x_np)
+        assert_same(name + " q_col", bits(q_col), eq)
+        assert_same(name + " s_col", bits(s_col), es)
+        assert_same(name + " dequant col", bits(bsq.mx_dequantize(q_col, s_col)),
+                    oracle.mx_dequantize(eq, es))
+
+
+def _check_nv(name, x_np, q, sb, st, y):
+    eq, esb, est = oracle.nv_quantize_per_token(x_np)
+    assert_same(name + " st", bits(st), est.view(np.uint32))
+    assert_same(name + " sb", bits(sb), esb)
+    assert_same(name + " q", bits(q), eq)
+    assert_same(name + " dequant", bits(y), oracle.nv_dequantize(eq, esb, est))
+
+
+def test_config1_mxfp8_rowwise_256x2048():
+    log("config1")
+    x = workloads.config1()["x"]
+    _check_mx("config1", x, to_dev(x), "rowwise")
+
+
+def test_config2_mxfp8_dual_8192x2048_and_dequant():
+    log("config2")
+    x = workloads.config2()["x"]
+    _check_mx("config2", x, to_dev(x), "both")
+
+
+def test_config3_nvfp4_grouped_131072x2048():
+    log("config3: generating")
+    cfg = workloads.config3()
+    x, off = cfg["x"], cfg["offsets"]
+    assert x.shape == (131072, 2048) and off.shape == (129,)
+    xd = to_dev(x)
+    q, sb, st, status = bsq.nv_quantize_nvfp4_per_token_grouped(xd, torch.from_numpy(off).cuda())
+    y = bsq.nv_dequantize(q, sb, st)
+    torch.cuda.synchronize()
+    assert int(status.item()) == bsq.BSQ_OK
+    log("config3: comparing")
+    _check_nv("config3", x, q, sb, st, y)
+
+
+def test_config4_weight_export_128_experts():
+    log("config4: generating")
+    cfg = workloads.config4()
+    for key, shape in (("gate_up", (196608, 2048)), ("down", (262144, 768))):
+        w = cfg[key]
+        assert w.shape == shape
+        wd = to_dev(w)
+        log("config4 %s: nvfp4" % key)
+        q, sb, st = bsq.nv_quantize_nvfp4_per_token(wd)
+        y = bsq.nv_dequantize(q, sb, st)
+        _check_nv("config4 " + key, w, q, sb, st, y)
+        del q, sb, st, y
+        log("config4 %s: mxfp8 rowwise" % key)
+        _check_mx("config4 " + key, w, wd, "rowwise")
+        del wd
+
+
+def test_config5_layer_step_stream():
+    log("config5: generating")
+    cfg = workloads.config5()
+    a, w, tok, off = cfg["a"], cfg["w"], cfg["token_idx"], cfg["offsets"]
+    assert a.shape == (65536, 2048) and w.shape == (2048, 6144) and tok.shape == (524288,)
+    ad, wd = to_dev(a), to_dev(w)
+    tokd = torch.from_numpy(tok).cuda()
+    xd = ad.index_select(0, tokd)                      # routed rows, gathered on the device
+    # the step: MX dual on A and W, NV grouped on X, then dequant of every output
+    a_q = bsq.mx_quantize_mxfp8(ad, "both")
+    w_q = bsq.mx_quantize_mxfp8(wd, "both")
+    q, sb, st, status = bsq.nv_quantize_nvfp4_per_token_grouped(xd, torch.from_numpy(off).cuda())
+    ya_r, ya_c = bsq.mx_dequantize(a_q[0], a_q[1]), bsq.mx_dequantize(a_q[2], a_q[3])
+    yw_r, yw_c = bsq.mx_dequantize(w_q[0], w_q[1]), bsq.mx_dequantize(w_q[2], w_q[3])
+    yx = bsq.nv_dequantize(q, sb, st)
+    torch.cuda.synchronize()
+    assert int(status.item()) == bsq.BSQ_OK
+
+    log("config5: comparing W")
+    ew = oracle.mx_quantize_rowwise(w), oracle.mx_quantize_colwise(w)
+    assert_same("W q_row", bits(w_q[0]), ew[0][0])
+    assert_same("W s_row", bits(w_q[1]), ew[0][1])
+    assert_same("W q_col", bits(w_q[2]), ew[1][0])
+    assert_same("W s_col", bits(w_q[3]), ew[1][1])
+    assert_same("W dequant row", bits(yw_r), oracle.mx_dequantize(*ew[0]))
+    assert_same("W dequant col", bits(yw_c), oracle.mx_dequantize(*ew[1]))
+
+    log("config5: comparing A")
+    er = oracle.mx_quantize_rowwise(a)
+    assert_same("A q_row", bits(a_q[0]), er[0])
+    assert_same("A s_row", bits(a_q[1]), er[1])
+    assert_same("A dequant row", bits(ya_r), oracle.mx_dequantize(*er))
+    del er
+    ec = oracle.mx_quantize_colwise(a)
+    assert_same("A q_col", bits(a_q[2]), ec[0])
+    assert_same("A s_col", bits(a_q[3]), ec[1])
+    assert_same("A dequant col", bits(ya_c), oracle.mx_dequantize(*ec))
+    del ec
+
+    log("config5: comparing sampled routed rows")
+    rows = np.sort(np.random.default_rng(55).choice(tok.size, 8192, replace=False))
+    rows_d = torch.from_numpy(rows).cuda()
+    x_s = a[tok[rows]]
+    eq, esb, est = oracle.nv_quantize_per_token(x_s)
+    assert_same("X st", bits(st.index_select(0, rows_d)), est.view(np.uint32))
+    assert_same("X sb", bits(sb.index_select(0, rows_d)), esb)
+    assert_same("X q", bits(q.index_select(0, rows_d)), eq)
+    assert_same("X dequant", bits(yx.index_select(0, rows_d)), oracle.nv_dequantize(eq, esb, est))
+    # duplicated tokens (a token routed to 8 experts) give byte-identical rows
+    first = {}
+    for i, t in enumerate(tok[:4096]):
+        first.setdefault(int(t), i)
+    pairs = [(first[int(t)], i) for i, t in enumerate(tok[:4096]) if first[int(t)] != i][:256]
+    if pairs:
+        i0 = torch.tensor([p[0] for p in pairs], device="cuda")
+        i1 = torch.tensor([p[1] for p in pairs], device="cuda")
+        assert torch.equal(q.index_select(0, i0), q.index_select(0, i1))
