@@ -57,7 +57,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample", type=int, default=8,
+    p.add_argument("--cpu-sample", type=int, default=1,
                    help="the CPU baseline runs 1/N of the step's rows")
     p.add_argument("--profile-pass", action="store_true",
                    help="short run for hardware-counter passes: one 1 GiB device copy (the "

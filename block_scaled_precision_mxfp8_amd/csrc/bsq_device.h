@@ -1,10 +1,10 @@
 // bsq_device.h -- device-side format codecs and wavefront helpers for gfx950 (CDNA4).
 //
-// Every conversion here is integer/bit arithmetic or a single IEEE binary32 operation, so
-// the results do not depend on any hardware conversion instruction.  The build disables
-// FMA contraction (-ffp-contract=off); binary32 denormals are kept (the default denormal
-// mode of HIP device code on gfx950), which the MXFP8 path relies on for BF16 subnormal
-// inputs.
+// Scale arithmetic is integer/bit manipulation or single IEEE binary32 operations; the
+// per-element conversions use the gfx950 conversion instructions wrapped below, in the
+// one way each of them matches the contract bit for bit.  The build disables FMA
+// contraction (-ffp-contract=off) and keeps binary32 denormals (the default denormal mode
+// of HIP device code on gfx950; subnormal scales and BF16 subnormal inputs rely on it).
 //
 // Formats (page "Towards Blackwell-native 8-bit and 4-bit RL", section "Format
 // background"): E4M3 = OCP E4M3FN, E8M0 = unsigned power of two, E2M1 = {0 .. 6}.
@@ -88,28 +88,56 @@ __device__ __forceinline__ float e4m3_decode_mag(uint32_t m) {
     return (e == 0u) ? sub : nrm;
 }
 
-// ----------------------------------------------------------------------------- E2M1
+// ----------------------------------------------------------------------------- gfx950 converts
+//
+// The scaled conversion instructions of gfx950 compute, with round-to-nearest-even,
+//   to FP8/FP4:   ENC(x / 2^floor(log2 scale))   (FP8: NaN beyond 448; FP4: saturates at 6)
+//   from FP8/FP4: DEC(code) * 2^floor(log2 scale)
+// The kernels only use them where that is exactly the contract: MXFP8 encode (scale is
+// the E8M0 power of two and |x / scale| <= 448 by construction), NVFP4 element encode
+// (scale 1.0 on the already multiplied binary32 value), MXFP8 decode to BF16, NVFP4
+// decode to binary32 (scale 1.0), and binary32 -> BF16.  The tests sweep each use
+// exhaustively against the CPU oracle: every BF16 input at every E8M0 scale through the
+// MXFP8 kernels, all 256 x 256 MXFP8 (code, scale) pairs through dequantization, and all
+// 2^32 binary32 inputs for the FP4 encode and the BF16 rounding helpers below.
 
-// E2M1 magnitude code of a >= 0 (binary32, not NaN): nearest of {0,.5,1,1.5,2,3,4,6},
-// ties to the even code, saturating at 6 (code 7).
-//  * a >= 1: round the mantissa to 1 bit on the bit pattern; code = (biased exponent -
-//    126) * 2 + mantissa bit, i.e. (bits >> 22) - 252 after rounding.
-//  * a < 1 (step 0.5): adding 2^22, whose binary32 ulp is 0.5, rounds a to a multiple of
-//    0.5 with round-to-nearest-even; the multiple (0, 1 or 2) is the code.
-__device__ __forceinline__ uint32_t e2m1_code(float a) {
-    uint32_t u = __float_as_uint(a);
-    uint32_t cn = ((u + 0x1FFFFFu + ((u >> 22) & 1u)) >> 22) - 252u;
-    uint32_t cs = __float_as_uint(a + 4194304.0f) - 0x4A800000u;
-    uint32_t c = (a < 1.0f) ? cs : cn;
-    return min(c, 7u);
+typedef short short2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// Four E4M3 codes (little-endian bytes) of the BF16 pairs w0 = (x0, x1), w1 = (x2, x3)
+// divided by `scale` (a power of two 2^(c-127); 2^-127 is the subnormal 0x00400000).
+__device__ __forceinline__ uint32_t cvt_e4m3x4_bf16(uint32_t w0, uint32_t w1, float scale) {
+    short2_t r = {0, 0};
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2_t, w0), scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2_t, w1), scale, true);
+    return __builtin_bit_cast(uint32_t, r);
 }
 
-// binary32 value of an E2M1 magnitude code 0..7 (exact).
-__device__ __forceinline__ float e2m1_decode_mag(uint32_t m) {
-    // codes >= 2 are normal: exponent field (m >> 1) + 126, mantissa bit m & 1 at bit 22,
-    // which is (m + 252) << 22; code 1 is 0.5 and code 0 is 0.
-    float nrm = __uint_as_float((m + 252u) << 22);
-    return (m >= 2u) ? nrm : (m == 1u ? 0.5f : 0.0f);
+// Byte `sel` of `old` replaced by the two E2M1 codes of a (low nibble) and b (high
+// nibble): nearest, ties to the even code, sign kept, saturating at 6.
+template <int sel>
+__device__ __forceinline__ uint32_t cvt_e2m1x2_f32(uint32_t old, float a, float b) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, sel);
+}
+
+// The two BF16 values (packed) of E4M3 codes in bytes 2*hi, 2*hi+1 of w times `scale`
+// (a power of two), rounded to nearest-even.  NaN codes come out as 0xFFC0.
+template <bool hi>
+__device__ __forceinline__ uint32_t cvt_bf16x2_e4m3(uint32_t w, float scale) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, hi));
+}
+
+// The two binary32 values of the E2M1 codes in byte `sel` of w (exact).
+template <int sel>
+__device__ __forceinline__ float2_t cvt_f32x2_e2m1(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, sel);
+}
+
+// BF16 pair of two binary32 values, round-to-nearest-even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_bf16x2_f32(float a, float b) {
+    float2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // ----------------------------------------------------------------------------- lanes

@@ -20,19 +20,16 @@ namespace bsq {
 
 // ----------------------------------------------------------------------------- encode
 
-// Two E4M3 codes (bits 0-7 and 8-15) of the BF16 pair w scaled by inv = 2^-e.  The
-// product is exact and at most 448 (the scale never clips), so no saturation is needed.
-__device__ __forceinline__ uint32_t mx_enc2(uint32_t w, float inv) {
-    float lo = fabsf(__uint_as_float(bf16_lo_bits(w))) * inv;
-    float hi = fabsf(__uint_as_float(bf16_hi_bits(w))) * inv;
-    uint32_t c0 = e4m3_code(lo) | ((w >> 8) & 0x80u);
-    uint32_t c1 = e4m3_code(hi) | ((w >> 24) & 0x80u);
-    return c0 | (c1 << 8);
+// Eight E4M3 codes of a 16-byte chunk of BF16 divided by the block scale 2^(c-127): the
+// quotient is exact and at most 448 (the scale never clips), where the gfx950 scaled
+// convert is exactly round-to-nearest-even of the quotient.
+__device__ __forceinline__ uint2 mx_enc8(const uint4& v, float scale) {
+    return make_uint2(cvt_e4m3x4_bf16(v.x, v.y, scale), cvt_e4m3x4_bf16(v.z, v.w, scale));
 }
 
-// Four E4M3 codes of two BF16 pairs, little-endian in one dword.
-__device__ __forceinline__ uint32_t mx_enc4(uint32_t w0, uint32_t w1, float inv) {
-    return mx_enc2(w0, inv) | (mx_enc2(w1, inv) << 16);
+// Dword d (0..3) of a 16-byte chunk; d is a compile-time constant after unrolling.
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int d) {
+    return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
 }
 
 // Magnitude maximum (BF16 bits) of the 8 BF16 values of a 16-byte chunk.
@@ -72,10 +69,7 @@ void mx_quant_rowwise_kernel(const uint4* __restrict__ x, uint2* __restrict__ q,
     for (int j = 0; j < ROW_SLOTS; ++j) {
         const uint32_t amax = quad_max(chunk_absmax(v[j]));
         const uint32_t code = e8m0_code_from_bf16_mag(amax);
-        const float inv = e8m0_inverse(code);
-        uint2 out;
-        out.x = mx_enc4(v[j].x, v[j].y, inv);
-        out.y = mx_enc4(v[j].z, v[j].w, inv);
+        const uint2 out = mx_enc8(v[j], e8m0_decode(code));
         const int64_t c = base + 64 * j + lane;
         if (c < n_chunks) q[c] = out;
         if ((lane & 3) == 0) lds_s[wave][16 * j + (lane >> 2)] = (uint8_t)code;
@@ -151,10 +145,7 @@ void mx_quant_tile_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
         for (int i = 0; i < 16; ++i) {
             const uint32_t amax = quad_max(chunk_absmax(v[i]));
             const uint32_t code = e8m0_code_from_bf16_mag(amax);
-            const float inv = e8m0_inverse(code);
-            uint2 out;
-            out.x = mx_enc4(v[i].x, v[i].y, inv);
-            out.y = mx_enc4(v[i].z, v[i].w, inv);
+            const uint2 out = mx_enc8(v[i], e8m0_decode(code));
             if (ok) {
                 *reinterpret_cast<uint2*>(q_row + (row0 + i) * K + col0) = out;
                 if ((c & 3) == 0) s_row[(row0 + i) * nb_row + (col0 >> 5)] = (uint8_t)code;
@@ -189,23 +180,19 @@ void mx_quant_tile_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
     for (int d = 0; d < 4; ++d) {
         const uint32_t code0 = e8m0_code_from_bf16_mag(cm[d] & 0xFFFFu);   // column 2d
         const uint32_t code1 = e8m0_code_from_bf16_mag(cm[d] >> 16);       // column 2d+1
-        const float inv0 = e8m0_inverse(code0);
-        const float inv1 = e8m0_inverse(code1);
+        const float sc0 = e8m0_decode(code0);
+        const float sc1 = e8m0_decode(code1);
+        // Column-major pairs (row i, row i+1) of one column, built with one byte permute
+        // each, so one scaled convert (one scale = the column's) encodes two rows.
         uint32_t a[4], b[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            uint32_t pa = 0u, pb = 0u;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t wv = (d == 0) ? v[4 * t + u].x : (d == 1) ? v[4 * t + u].y
-                                  : (d == 2) ? v[4 * t + u].z : v[4 * t + u].w;
-                const float lo = fabsf(__uint_as_float(bf16_lo_bits(wv))) * inv0;
-                const float hi = fabsf(__uint_as_float(bf16_hi_bits(wv))) * inv1;
-                pa |= (e4m3_code(lo) | ((wv >> 8) & 0x80u)) << (8 * u);
-                pb |= (e4m3_code(hi) | ((wv >> 24) & 0x80u)) << (8 * u);
-            }
-            a[t] = pa;
-            b[t] = pb;
+            const uint32_t r0 = dword_of(v[4 * t + 0], d), r1 = dword_of(v[4 * t + 1], d);
+            const uint32_t r2 = dword_of(v[4 * t + 2], d), r3 = dword_of(v[4 * t + 3], d);
+            a[t] = cvt_e4m3x4_bf16(__builtin_amdgcn_perm(r1, r0, 0x05040100u),
+                                   __builtin_amdgcn_perm(r3, r2, 0x05040100u), sc0);
+            b[t] = cvt_e4m3x4_bf16(__builtin_amdgcn_perm(r1, r0, 0x07060302u),
+                                   __builtin_amdgcn_perm(r3, r2, 0x07060302u), sc1);
         }
         if (ok) {
             const int64_t ka = col0 + 2 * d;
@@ -227,19 +214,31 @@ void mx_quant_tile_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
 constexpr int DQ_SLOTS = 4;
 constexpr int DQ_WAVES = 4;
 
-__device__ __forceinline__ uint32_t mx_dec1(uint32_t code, float scale, bool nan_scale) {
-    const uint32_t mag = code & 0x7Fu;
-    const float v = e4m3_decode_mag(mag) * scale;                // exact, may be +inf
-    const uint32_t u = rne_bf16(__float_as_uint(v)) | ((code & 0x80u) << 8);
-    return (mag == 0x7Fu || nan_scale) ? 0x7FC0u : u;
+// Eight BF16 (16 bytes) of the eight E4M3 codes in (w0, w1) times the block scale.  The
+// product is exact in binary32 for every finite code and scale, and the convert rounds it
+// to BF16 to nearest-even (overflow to infinity).  NaN codes (0x7F, 0xFF) and the NaN
+// scale 0xFF give 0x7FC0; the hardware writes 0xFFC0 for a NaN code, so those rare
+// chunks are patched.
+__device__ __forceinline__ uint32_t fix_nan_pair(uint32_t y, uint32_t codes2) {
+    const uint32_t lo = ((codes2 & 0x7Fu) == 0x7Fu) ? 0x7FC0u : (y & 0xFFFFu);
+    const uint32_t hi = (((codes2 >> 8) & 0x7Fu) == 0x7Fu) ? 0x7FC00000u : (y & 0xFFFF0000u);
+    return lo | hi;
 }
 
-__device__ __forceinline__ uint4 mx_dec8(uint32_t w0, uint32_t w1, float scale, bool nan_scale) {
-    uint4 o;
-    o.x = mx_dec1(w0 & 0xFF, scale, nan_scale) | (mx_dec1((w0 >> 8) & 0xFF, scale, nan_scale) << 16);
-    o.y = mx_dec1((w0 >> 16) & 0xFF, scale, nan_scale) | (mx_dec1(w0 >> 24, scale, nan_scale) << 16);
-    o.z = mx_dec1(w1 & 0xFF, scale, nan_scale) | (mx_dec1((w1 >> 8) & 0xFF, scale, nan_scale) << 16);
-    o.w = mx_dec1((w1 >> 16) & 0xFF, scale, nan_scale) | (mx_dec1(w1 >> 24, scale, nan_scale) << 16);
+__device__ __forceinline__ uint4 mx_dec8(uint32_t w0, uint32_t w1, uint32_t c) {
+    const float scale = e8m0_decode(c);
+    uint4 o = make_uint4(cvt_bf16x2_e4m3<false>(w0, scale), cvt_bf16x2_e4m3<true>(w0, scale),
+                         cvt_bf16x2_e4m3<false>(w1, scale), cvt_bf16x2_e4m3<true>(w1, scale));
+    const uint32_t nan0 = ((w0 & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+    const uint32_t nan1 = ((w1 & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+    if (c == 255u) {
+        o = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+    } else if ((nan0 | nan1) != 0u) {
+        o.x = fix_nan_pair(o.x, w0);
+        o.y = fix_nan_pair(o.y, w0 >> 16);
+        o.z = fix_nan_pair(o.z, w1);
+        o.w = fix_nan_pair(o.w, w1 >> 16);
+    }
     return o;
 }
 
@@ -262,11 +261,11 @@ void mx_dequant_kernel(const uint4* __restrict__ q, const uint8_t* __restrict__ 
 #pragma unroll
     for (int j = 0; j < DQ_SLOTS; ++j) {
         const int64_t c = base + 64 * j + lane;
-        const float scale = e8m0_decode(sc[j]);
-        const bool nan_scale = sc[j] == 255u;
+        const uint4 o0 = mx_dec8(w[j].x, w[j].y, sc[j]);
+        const uint4 o1 = mx_dec8(w[j].z, w[j].w, sc[j]);
         if (c < n_chunks) {
-            y[2 * c] = mx_dec8(w[j].x, w[j].y, scale, nan_scale);
-            y[2 * c + 1] = mx_dec8(w[j].z, w[j].w, scale, nan_scale);
+            y[2 * c] = o0;
+            y[2 * c + 1] = o1;
         }
     }
 }

@@ -22,18 +22,19 @@
 namespace bsq {
 
 // Eight E2M1 codes (one nibble each, element 2j in the low nibble of byte j) of the
-// BF16 values of a 16-byte chunk multiplied by f: q = ENC_E2M1(fl(x * f)).  The sign of
-// fl(x * f) is the sign of x because f >= 0.
-__device__ __forceinline__ uint32_t nv_enc2(uint32_t w, float f) {
-    const float lo = fabsf(__uint_as_float(bf16_lo_bits(w))) * f;
-    const float hi = fabsf(__uint_as_float(bf16_hi_bits(w))) * f;
-    const uint32_t c0 = e2m1_code(lo) | ((w >> 12) & 0x8u);
-    const uint32_t c1 = e2m1_code(hi) | ((w >> 28) & 0x8u);
-    return c0 | (c1 << 4);
-}
+// BF16 values of a 16-byte chunk multiplied by f: q = ENC_E2M1(fl(x * f)).  The binary32
+// product is rounded by the multiply; the FP4 convert (scale 1.0) then rounds it to the
+// nearest E2M1 value, ties to the even code, keeping the sign.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(bf16_lo_bits(w)); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(bf16_hi_bits(w)); }
 
 __device__ __forceinline__ uint32_t nv_enc8(const uint4& v, float f) {
-    return nv_enc2(v.x, f) | (nv_enc2(v.y, f) << 8) | (nv_enc2(v.z, f) << 16) | (nv_enc2(v.w, f) << 24);
+    uint32_t r = 0u;
+    r = cvt_e2m1x2_f32<0>(r, bf16_lo(v.x) * f, bf16_hi(v.x) * f);
+    r = cvt_e2m1x2_f32<1>(r, bf16_lo(v.y) * f, bf16_hi(v.y) * f);
+    r = cvt_e2m1x2_f32<2>(r, bf16_lo(v.z) * f, bf16_hi(v.z) * f);
+    r = cvt_e2m1x2_f32<3>(r, bf16_lo(v.w) * f, bf16_hi(v.w) * f);
+    return r;
 }
 
 __device__ __forceinline__ uint32_t chunk_absmax8(const uint4& v) {
@@ -167,11 +168,24 @@ void nv_quant_rows_long_kernel(const uint4* __restrict__ x, uint32_t* __restrict
 constexpr int NVDQ_SLOTS = 4;
 constexpr int NVDQ_WAVES = 4;
 
-__device__ __forceinline__ uint32_t nv_dec1(uint32_t nib, float bscale, float s_t) {
-    const float e = e2m1_decode_mag(nib & 7u);
-    const float inner = ((nib & 8u) ? -e : e) * bscale;      // exact (<= 6 significant bits)
-    const uint32_t u = __float_as_uint(inner * s_t);          // one binary32 rounding
-    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC0u : rne_bf16(u) & 0xFFFFu;
+// Two BF16 (one dword) of the E2M1 codes in byte `sel` of `word`:
+// RNE_BF16(fl((DEC_E2M1(q) * DEC_E4M3(sb)) * s_t)); the inner product is exact.
+template <int sel>
+__device__ __forceinline__ uint32_t nv_dec2(uint32_t word, float bscale, float s_t) {
+    const float2_t e = cvt_f32x2_e2m1<sel>(word);
+    return cvt_bf16x2_f32((e.x * bscale) * s_t, (e.y * bscale) * s_t);
+}
+
+// The same with NaN results written as 0x7FC0 (only reachable when the block scale is a
+// NaN code or s_t is not finite).
+template <int sel>
+__device__ __forceinline__ uint32_t nv_dec2_nan(uint32_t word, float bscale, float s_t) {
+    const float2_t e = cvt_f32x2_e2m1<sel>(word);
+    const float p0 = (e.x * bscale) * s_t, p1 = (e.y * bscale) * s_t;
+    const uint32_t y = cvt_bf16x2_f32(p0, p1);
+    const uint32_t lo = (p0 != p0) ? 0x7FC0u : (y & 0xFFFFu);
+    const uint32_t hi = (p1 != p1) ? 0x7FC00000u : (y & 0xFFFF0000u);
+    return lo | hi;
 }
 
 __global__ __launch_bounds__(64 * NVDQ_WAVES)
@@ -204,12 +218,18 @@ void nv_dequant_kernel(const uint2* __restrict__ q, const uint8_t* __restrict__ 
         const float bm = e4m3_decode_mag(mag);
         const float bscale = (mag == 0x7Fu) ? __uint_as_float(0x7FC00000u)
                                             : ((code[j] & 0x80u) ? -bm : bm);
+        const float st = s_t[j];
         uint32_t o[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t word = (i < 4) ? w[j].x : w[j].y;
-            const uint32_t byte = (word >> (8 * (i & 3))) & 0xFFu;
-            o[i] = nv_dec1(byte & 0xFu, bscale, s_t[j]) | (nv_dec1(byte >> 4, bscale, s_t[j]) << 16);
+        if (mag != 0x7Fu && fabsf(st) <= FLT_MAX) {
+            o[0] = nv_dec2<0>(w[j].x, bscale, st); o[1] = nv_dec2<1>(w[j].x, bscale, st);
+            o[2] = nv_dec2<2>(w[j].x, bscale, st); o[3] = nv_dec2<3>(w[j].x, bscale, st);
+            o[4] = nv_dec2<0>(w[j].y, bscale, st); o[5] = nv_dec2<1>(w[j].y, bscale, st);
+            o[6] = nv_dec2<2>(w[j].y, bscale, st); o[7] = nv_dec2<3>(w[j].y, bscale, st);
+        } else {
+            o[0] = nv_dec2_nan<0>(w[j].x, bscale, st); o[1] = nv_dec2_nan<1>(w[j].x, bscale, st);
+            o[2] = nv_dec2_nan<2>(w[j].x, bscale, st); o[3] = nv_dec2_nan<3>(w[j].x, bscale, st);
+            o[4] = nv_dec2_nan<0>(w[j].y, bscale, st); o[5] = nv_dec2_nan<1>(w[j].y, bscale, st);
+            o[6] = nv_dec2_nan<2>(w[j].y, bscale, st); o[7] = nv_dec2_nan<3>(w[j].y, bscale, st);
         }
         if (b < n_blocks) {
             y[2 * b] = make_uint4(o[0], o[1], o[2], o[3]);

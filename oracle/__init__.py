@@ -88,6 +88,10 @@ def lib() -> ctypes.CDLL:
         for name in ("oracle_enc_e4m3_array", "oracle_enc_e2m1_array", "oracle_rne_bf16_array"):
             getattr(L, name).restype = None
             getattr(L, name).argtypes = [P, I64, P]
+        L.oracle_enc_e2m1_f32_range.restype = None
+        L.oracle_enc_e2m1_f32_range.argtypes = [ctypes.c_uint32, I64, P]
+        L.oracle_rne_bf16_f32_range.restype = None
+        L.oracle_rne_bf16_f32_range.argtypes = [ctypes.c_uint32, I64, P]
         L.oracle_max_threads.restype = ctypes.c_int
         L.oracle_max_threads.argtypes = []
         _lib = L
@@ -252,6 +256,20 @@ def nv_dequantize(q: np.ndarray, sb: np.ndarray, st: np.ndarray) -> np.ndarray:
     y = np.empty((R, K), np.uint16)
     lib().oracle_nv_dequantize(_ptr(q), _ptr(sb), _ptr(st), R, K, _ptr(y))
     return y
+
+
+def enc_e2m1_f32_range(start: int, n: int) -> np.ndarray:
+    """E2M1 codes of the binary32 patterns start .. start+n-1 (NaN patterns give 0)."""
+    out = np.empty(n, np.uint8)
+    lib().oracle_enc_e2m1_f32_range(start, n, _ptr(out))
+    return out
+
+
+def rne_bf16_f32_range(start: int, n: int) -> np.ndarray:
+    """BF16 patterns of the binary32 patterns start .. start+n-1 (NaN gives 0x7FC0)."""
+    out = np.empty(n, np.uint16)
+    lib().oracle_rne_bf16_f32_range(start, n, _ptr(out))
+    return out
 
 
 def max_threads() -> int:

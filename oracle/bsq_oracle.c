@@ -354,6 +354,29 @@ void oracle_rne_bf16_array(const double* v, int64_t n, uint16_t* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_rne_bf16(v[i]);
 }
 
+/* The encoders applied to every binary32 bit pattern start, start+1, ..., start+n-1 (for
+ * exhaustive sweeps of a conversion over all 2^32 inputs, in chunks).  Inputs that are
+ * NaN get the output 0 (E2M1) / 0x7FC0 (BF16) and are skipped by the sweeps. */
+static double f32_from_bits(uint32_t b) {
+    float f;
+    memcpy(&f, &b, sizeof f);
+    return (double)f;
+}
+
+void oracle_enc_e2m1_f32_range(uint32_t start, int64_t n, uint8_t* out) {
+    build_tables();
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        double v = f32_from_bits(start + (uint32_t)i);
+        out[i] = isnan(v) ? 0 : oracle_enc_e2m1(v);
+    }
+}
+
+void oracle_rne_bf16_f32_range(uint32_t start, int64_t n, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_rne_bf16(f32_from_bits(start + (uint32_t)i));
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
     extern int omp_get_max_threads(void);
