@@ -140,6 +140,31 @@ __device__ __forceinline__ uint32_t cvt_bf16x2_f32(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// ----------------------------------------------------------------------------- division
+
+// Exact n / d for every 32-bit n and 1 <= d < 2^32 by one multiply-high: with
+// c = ceil(2^64 / d), floor(n * c / 2^64) == floor(n / d) because c * d - 2^64 < d makes the
+// error term n * (c - 2^64/d) / 2^64 < 2^32 / 2^64 < 1 / d.  The 96-bit product's top
+// bits are m_hi * n + mulhi(m_lo, n), shifted by 32.  d == 1 is passed through.
+struct FastDiv {
+    uint32_t m_lo, m_hi, d;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    const uint64_t c = (d <= 1u) ? 0u : (UINT64_MAX / d + 1u);
+    f.m_lo = (uint32_t)c;
+    f.m_hi = (uint32_t)(c >> 32);
+    return f;
+}
+
+__device__ __forceinline__ uint32_t fastdiv(uint32_t n, const FastDiv& f) {
+    if (f.d == 1u) return n;
+    const uint64_t t = (uint64_t)f.m_hi * n + (uint64_t)__umulhi(f.m_lo, n);
+    return (uint32_t)(t >> 32);
+}
+
 // ----------------------------------------------------------------------------- lanes
 
 // DPP quad permutations: value of the lane (i ^ 1) and (i ^ 2) within each quad.

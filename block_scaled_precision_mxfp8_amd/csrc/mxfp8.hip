@@ -115,6 +115,11 @@ void mx_quant_tile_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                           uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
                           uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
                           int64_t col_groups, int64_t n_wg) {
+    // Scale codes of the workgroup tile (128 rows x 256 columns), gathered so they leave
+    // as one 8-byte store per row (rowwise scales) and one 4-byte store per column
+    // (columnwise scales) instead of one byte store per block.
+    __shared__ __align__(16) uint8_t lds_srow[TILE_ROWS][2 * TILE_WAVES];
+    __shared__ __align__(16) uint8_t lds_scol[TILE_WAVES * TILE_COLS][TILE_ROWS / 32];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 3;
@@ -123,8 +128,8 @@ void mx_quant_tile_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
     int64_t w = blockIdx.x;
     if ((n_wg & 7) == 0) w = (w & 7) * (n_wg >> 3) + (w >> 3);   // XCD-contiguous ranges
     const int64_t r0 = (w / col_groups) * TILE_ROWS;
-    const int64_t k0 = ((w % col_groups) * TILE_WAVES + wave) * TILE_COLS;
-    if (k0 >= K) return;
+    const int64_t kw = (w % col_groups) * (TILE_WAVES * TILE_COLS);  // workgroup's first column
+    const int64_t k0 = kw + wave * TILE_COLS;
 
     const int64_t row0 = r0 + 16 * g;          // first of this lane's 16 rows
     const int64_t col0 = k0 + 8 * c;           // first of this lane's 8 columns
@@ -140,16 +145,13 @@ void mx_quant_tile_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
 
     // ---- rowwise copy: each row of the lane, block = quad of lanes
     if (ROW) {
-        const int64_t nb_row = K >> 5;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const uint32_t amax = quad_max(chunk_absmax(v[i]));
             const uint32_t code = e8m0_code_from_bf16_mag(amax);
             const uint2 out = mx_enc8(v[i], e8m0_decode(code));
-            if (ok) {
-                *reinterpret_cast<uint2*>(q_row + (row0 + i) * K + col0) = out;
-                if ((c & 3) == 0) s_row[(row0 + i) * nb_row + (col0 >> 5)] = (uint8_t)code;
-            }
+            if (ok) *reinterpret_cast<uint2*>(q_row + (row0 + i) * K + col0) = out;
+            if ((c & 3) == 0) lds_srow[16 * g + i][2 * wave + (c >> 2)] = (uint8_t)code;
         }
         // The column pass below re-derives its FP32 operands from the packed tile; this
         // empty register barrier stops the compiler from instead keeping the row pass's
@@ -175,7 +177,6 @@ void mx_quant_tile_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
         u16x2 b = __builtin_bit_cast(u16x2, other);
         cm[d] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
     }
-    const int64_t nb_col = M >> 5;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         const uint32_t code0 = e8m0_code_from_bf16_mag(cm[d] & 0xFFFFu);   // column 2d
@@ -187,44 +188,71 @@ void mx_quant_tile_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
         uint32_t a[4], b[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const uint32_t r0 = dword_of(v[4 * t + 0], d), r1 = dword_of(v[4 * t + 1], d);
-            const uint32_t r2 = dword_of(v[4 * t + 2], d), r3 = dword_of(v[4 * t + 3], d);
-            a[t] = cvt_e4m3x4_bf16(__builtin_amdgcn_perm(r1, r0, 0x05040100u),
-                                   __builtin_amdgcn_perm(r3, r2, 0x05040100u), sc0);
-            b[t] = cvt_e4m3x4_bf16(__builtin_amdgcn_perm(r1, r0, 0x07060302u),
-                                   __builtin_amdgcn_perm(r3, r2, 0x07060302u), sc1);
+            const uint32_t r0w = dword_of(v[4 * t + 0], d), r1w = dword_of(v[4 * t + 1], d);
+            const uint32_t r2w = dword_of(v[4 * t + 2], d), r3w = dword_of(v[4 * t + 3], d);
+            a[t] = cvt_e4m3x4_bf16(__builtin_amdgcn_perm(r1w, r0w, 0x05040100u),
+                                   __builtin_amdgcn_perm(r3w, r2w, 0x05040100u), sc0);
+            b[t] = cvt_e4m3x4_bf16(__builtin_amdgcn_perm(r1w, r0w, 0x07060302u),
+                                   __builtin_amdgcn_perm(r3w, r2w, 0x07060302u), sc1);
         }
         if (ok) {
             const int64_t ka = col0 + 2 * d;
             *reinterpret_cast<uint4*>(q_col + ka * M + row0) = make_uint4(a[0], a[1], a[2], a[3]);
             *reinterpret_cast<uint4*>(q_col + (ka + 1) * M + row0) = make_uint4(b[0], b[1], b[2], b[3]);
-            if ((g & 1) == 0) {
-                s_col[ka * nb_col + (row0 >> 5)] = (uint8_t)code0;
-                s_col[(ka + 1) * nb_col + (row0 >> 5)] = (uint8_t)code1;
-            }
+        }
+        if ((g & 1) == 0) {
+            lds_scol[wave * TILE_COLS + 8 * c + 2 * d][g >> 1] = (uint8_t)code0;
+            lds_scol[wave * TILE_COLS + 8 * c + 2 * d + 1][g >> 1] = (uint8_t)code1;
+        }
+    }
+
+    __syncthreads();
+    const int t = threadIdx.x;
+    // rowwise scales: thread t < 128 writes row r0 + t's 8 bytes (blocks kw/32 .. +7)
+    if (ROW && t < TILE_ROWS && r0 + t < M) {
+        const int64_t nb_row = K >> 5;
+        const int64_t b0 = kw >> 5;
+        const int nb = (int)min((int64_t)(2 * TILE_WAVES), nb_row - b0);
+        uint8_t* dst = s_row + (r0 + t) * nb_row + b0;
+        if (nb == 2 * TILE_WAVES && (nb_row & 7) == 0) {
+            *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(lds_srow[t]);
+        } else {
+            for (int i = 0; i < nb; ++i) dst[i] = lds_srow[t][i];
+        }
+    }
+    // columnwise scales: thread t writes column kw + t's 4 bytes (row blocks r0/32 .. +3)
+    if (kw + t < K) {
+        const int64_t nb_col = M >> 5;
+        const int64_t b0 = r0 >> 5;
+        const int nb = (int)min((int64_t)(TILE_ROWS / 32), nb_col - b0);
+        uint8_t* dst = s_col + (kw + t) * nb_col + b0;
+        if (nb == TILE_ROWS / 32 && (nb_col & 3) == 0) {
+            *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(lds_scol[t]);
+        } else {
+            for (int i = 0; i < nb; ++i) dst[i] = lds_scol[t][i];
         }
     }
 }
 
 // ----------------------------------------------------------------------------- dequant
 
-// MXFP8 -> BF16 in the stored layout, again a 1-D stream: element i uses scale i/32.
-// Lane l of slot j owns the 16 codes of chunk tile*64*DQ_SLOTS + 64*j + l (half a block)
-// and writes 32 bytes of BF16.
-constexpr int DQ_SLOTS = 4;
-constexpr int DQ_WAVES = 4;
+// MXFP8 -> BF16 in the stored layout, a 1-D stream: element i uses scale i/32.  Thread t of
+// a workgroup owns, in slot j, the 8 codes of chunk blockIdx*256*DQ_SLOTS + 256 j + t and
+// writes their 16 bytes of BF16, so every load instruction reads 512 contiguous bytes
+// and every store instruction writes 1 KiB contiguous; 4 neighbouring lanes share a scale.
+constexpr int DQ_SLOTS = 2;
 
-// Eight BF16 (16 bytes) of the eight E4M3 codes in (w0, w1) times the block scale.  The
-// product is exact in binary32 for every finite code and scale, and the convert rounds it
-// to BF16 to nearest-even (overflow to infinity).  NaN codes (0x7F, 0xFF) and the NaN
-// scale 0xFF give 0x7FC0; the hardware writes 0xFFC0 for a NaN code, so those rare
-// chunks are patched.
 __device__ __forceinline__ uint32_t fix_nan_pair(uint32_t y, uint32_t codes2) {
     const uint32_t lo = ((codes2 & 0x7Fu) == 0x7Fu) ? 0x7FC0u : (y & 0xFFFFu);
     const uint32_t hi = (((codes2 >> 8) & 0x7Fu) == 0x7Fu) ? 0x7FC00000u : (y & 0xFFFF0000u);
     return lo | hi;
 }
 
+// Eight BF16 (16 bytes) of the eight E4M3 codes in (w0, w1) times the block scale.  The
+// product is exact in binary32 for every finite code and scale, and the convert rounds it
+// to BF16 to nearest-even (overflow to infinity).  NaN codes (0x7F, 0xFF) and the NaN
+// scale 0xFF give 0x7FC0; the hardware writes 0xFFC0 for a NaN code, so those rare
+// chunks are patched.
 __device__ __forceinline__ uint4 mx_dec8(uint32_t w0, uint32_t w1, uint32_t c) {
     const float scale = e8m0_decode(c);
     uint4 o = make_uint4(cvt_bf16x2_e4m3<false>(w0, scale), cvt_bf16x2_e4m3<true>(w0, scale),
@@ -242,31 +270,24 @@ __device__ __forceinline__ uint4 mx_dec8(uint32_t w0, uint32_t w1, uint32_t c) {
     return o;
 }
 
-__global__ __launch_bounds__(64 * DQ_WAVES)
-void mx_dequant_kernel(const uint4* __restrict__ q, const uint8_t* __restrict__ s,
+__global__ __launch_bounds__(256)
+void mx_dequant_kernel(const uint2* __restrict__ q, const uint8_t* __restrict__ s,
                        uint4* __restrict__ y, int64_t n_chunks) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t base = ((int64_t)blockIdx.x * DQ_WAVES + wave) * (64 * DQ_SLOTS);
-    if (base >= n_chunks) return;
-    uint4 w[DQ_SLOTS];
+    const int64_t base = (int64_t)blockIdx.x * (256 * DQ_SLOTS) + threadIdx.x;
+    uint2 w[DQ_SLOTS];
     uint32_t sc[DQ_SLOTS];
 #pragma unroll
     for (int j = 0; j < DQ_SLOTS; ++j) {
-        const int64_t c = base + 64 * j + lane;
+        const int64_t c = base + 256 * j;
         const bool ok = c < n_chunks;
-        w[j] = ok ? q[c] : make_uint4(0u, 0u, 0u, 0u);
-        sc[j] = ok ? s[c >> 1] : 0u;
+        w[j] = ok ? q[c] : make_uint2(0u, 0u);
+        sc[j] = ok ? s[c >> 2] : 0u;
     }
 #pragma unroll
     for (int j = 0; j < DQ_SLOTS; ++j) {
-        const int64_t c = base + 64 * j + lane;
-        const uint4 o0 = mx_dec8(w[j].x, w[j].y, sc[j]);
-        const uint4 o1 = mx_dec8(w[j].z, w[j].w, sc[j]);
-        if (c < n_chunks) {
-            y[2 * c] = o0;
-            y[2 * c + 1] = o1;
-        }
+        const int64_t c = base + 256 * j;
+        const uint4 o = mx_dec8(w[j].x, w[j].y, sc[j]);
+        if (c < n_chunks) y[c] = o;
     }
 }
 
@@ -300,11 +321,10 @@ hipError_t launch_mx_quant(const void* x, int64_t M, int64_t K, int mode,
 
 hipError_t launch_mx_dequant(const void* q, const void* s, int64_t rows, int64_t cols,
                              void* y, hipStream_t stream) {
-    const int64_t n_chunks = rows * cols / 16;
-    const int64_t tiles = (n_chunks + 64 * DQ_SLOTS - 1) / (64 * DQ_SLOTS);
-    const int64_t grid = (tiles + DQ_WAVES - 1) / DQ_WAVES;
-    hipLaunchKernelGGL(mx_dequant_kernel, dim3((unsigned)grid), dim3(64 * DQ_WAVES), 0, stream,
-                       (const uint4*)q, (const uint8_t*)s, (uint4*)y, n_chunks);
+    const int64_t n_chunks = rows * cols / 8;
+    const int64_t grid = (n_chunks + 256 * DQ_SLOTS - 1) / (256 * DQ_SLOTS);
+    hipLaunchKernelGGL(mx_dequant_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const uint2*)q, (const uint8_t*)s, (uint4*)y, n_chunks);
     return hipGetLastError();
 }
 

@@ -106,16 +106,41 @@ void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
 
     uint32_t* qr = q + row * cpr;                     // 4 bytes of q per chunk
     uint8_t* sbr = sb + row * (K >> 4);
+    const bool odd = (lane & 1) != 0;
+    // Slots are taken two at a time: the two lanes of a block pair hold both blocks'
+    // maxima, the even lane works out slot j's scale and multiplier, the odd lane slot
+    // j+1's, and they swap results with one DPP move each (the two IEEE divisions per
+    // block are done once, not twice).
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-        const int64_t ch = 64 * j + lane;
-        const uint32_t amax_b = pair_max(chunk_absmax8(v[j]));
+    for (int j = 0; j < NS; j += 2) {
+        const bool two = j + 1 < NS;
+        const uint32_t a0 = pair_max(chunk_absmax8(v[j]));
+        const uint32_t a1 = two ? pair_max(chunk_absmax8(v[j + 1])) : 0u;
         float f;
-        const uint32_t code = nv_block_scale(amax_b, s_t, p, f);
-        const uint32_t packed = nv_enc8(v[j], f);
-        if (ch < cpr) {
-            qr[ch] = packed;
-            if ((lane & 1) == 0) sbr[ch >> 1] = (uint8_t)code;
+        const uint32_t code = nv_block_scale((two && odd) ? a1 : a0, s_t, p, f);
+        uint32_t code0 = code, code1 = code;
+        float f0 = f, f1 = f;
+        if (two) {
+            const uint32_t oc = dpp_xor1(code);
+            const float of = __uint_as_float(dpp_xor1(__float_as_uint(f)));
+            code0 = odd ? oc : code;
+            f0 = odd ? of : f;
+            code1 = odd ? code : oc;
+            f1 = odd ? f : of;
+        }
+        const int64_t ch0 = 64 * j + lane;
+        const uint32_t packed0 = nv_enc8(v[j], f0);
+        if (ch0 < cpr) {
+            qr[ch0] = packed0;
+            if (!odd) sbr[ch0 >> 1] = (uint8_t)code0;
+        }
+        if (two) {
+            const int64_t ch1 = 64 * (j + 1) + lane;
+            const uint32_t packed1 = nv_enc8(v[j + 1], f1);
+            if (ch1 < cpr) {
+                qr[ch1] = packed1;
+                if (!odd) sbr[ch1 >> 1] = (uint8_t)code1;
+            }
         }
     }
     if (lane == 0) st[row] = s_t;
@@ -163,13 +188,15 @@ void nv_quant_rows_long_kernel(const uint4* __restrict__ x, uint32_t* __restrict
 
 // ----------------------------------------------------------------------------- dequant
 
-// NVFP4 -> BF16: lane l of slot j owns one 16-element block (8 bytes of q) and writes
-// 32 bytes of BF16.  y = RNE_BF16(fl(exact(DEC_E2M1(q) DEC_E4M3(sb)) s_t)).
-constexpr int NVDQ_SLOTS = 4;
-constexpr int NVDQ_WAVES = 4;
+// NVFP4 -> BF16, a 1-D stream over half blocks (8 elements = 4 bytes of q = 16 bytes of
+// BF16): thread t of a workgroup owns half block blockIdx*256*NVDQ_SLOTS + 256 j + t in
+// slot j, so loads read 256 contiguous bytes and stores write 1 KiB contiguous per
+// instruction.  The row of half block h is h / (K/8), an exact multiply-high division.
+// y = RNE_BF16(fl(exact(DEC_E2M1(q) DEC_E4M3(sb)) s_t)).
+constexpr int NVDQ_SLOTS = 2;
 
-// Two BF16 (one dword) of the E2M1 codes in byte `sel` of `word`:
-// RNE_BF16(fl((DEC_E2M1(q) * DEC_E4M3(sb)) * s_t)); the inner product is exact.
+// Two BF16 (one dword) of the E2M1 codes in byte `sel` of `word`; the inner product is
+// exact, the product with s_t is one binary32 rounding, the convert is RNE to BF16.
 template <int sel>
 __device__ __forceinline__ uint32_t nv_dec2(uint32_t word, float bscale, float s_t) {
     const float2_t e = cvt_f32x2_e2m1<sel>(word);
@@ -188,53 +215,38 @@ __device__ __forceinline__ uint32_t nv_dec2_nan(uint32_t word, float bscale, flo
     return lo | hi;
 }
 
-__global__ __launch_bounds__(64 * NVDQ_WAVES)
-void nv_dequant_kernel(const uint2* __restrict__ q, const uint8_t* __restrict__ sb,
+__global__ __launch_bounds__(256)
+void nv_dequant_kernel(const uint32_t* __restrict__ q, const uint8_t* __restrict__ sb,
                        const float* __restrict__ st, uint4* __restrict__ y,
-                       int64_t n_blocks, int64_t blocks_per_row, double inv_bpr) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t base = ((int64_t)blockIdx.x * NVDQ_WAVES + wave) * (64 * NVDQ_SLOTS);
-    if (base >= n_blocks) return;
-    uint2 w[NVDQ_SLOTS];
-    uint32_t code[NVDQ_SLOTS];
+                       uint32_t n_half, FastDiv halves_per_row) {
+    const uint32_t base = blockIdx.x * (256u * NVDQ_SLOTS) + threadIdx.x;
+    uint32_t w[NVDQ_SLOTS], code[NVDQ_SLOTS];
     float s_t[NVDQ_SLOTS];
 #pragma unroll
     for (int j = 0; j < NVDQ_SLOTS; ++j) {
-        const int64_t b = base + 64 * j + lane;
-        const bool ok = b < n_blocks;
-        // row = b / blocks_per_row from a binary64 estimate, corrected by one step each way
-        int64_t r = (int64_t)((double)b * inv_bpr);
-        if ((r + 1) * blocks_per_row <= b) ++r;
-        if (r * blocks_per_row > b) --r;
-        w[j] = ok ? q[b] : make_uint2(0u, 0u);
-        code[j] = ok ? sb[b] : 0u;
-        s_t[j] = ok ? st[r] : 0.0f;
+        const uint32_t h = base + 256u * j;
+        const bool ok = h < n_half;
+        w[j] = ok ? q[h] : 0u;
+        code[j] = ok ? sb[h >> 1] : 0u;
+        s_t[j] = ok ? st[fastdiv(h, halves_per_row)] : 0.0f;
     }
 #pragma unroll
     for (int j = 0; j < NVDQ_SLOTS; ++j) {
-        const int64_t b = base + 64 * j + lane;
+        const uint32_t h = base + 256u * j;
         const uint32_t mag = code[j] & 0x7Fu;
         const float bm = e4m3_decode_mag(mag);
         const float bscale = (mag == 0x7Fu) ? __uint_as_float(0x7FC00000u)
                                             : ((code[j] & 0x80u) ? -bm : bm);
-        const float st = s_t[j];
-        uint32_t o[8];
-        if (mag != 0x7Fu && fabsf(st) <= FLT_MAX) {
-            o[0] = nv_dec2<0>(w[j].x, bscale, st); o[1] = nv_dec2<1>(w[j].x, bscale, st);
-            o[2] = nv_dec2<2>(w[j].x, bscale, st); o[3] = nv_dec2<3>(w[j].x, bscale, st);
-            o[4] = nv_dec2<0>(w[j].y, bscale, st); o[5] = nv_dec2<1>(w[j].y, bscale, st);
-            o[6] = nv_dec2<2>(w[j].y, bscale, st); o[7] = nv_dec2<3>(w[j].y, bscale, st);
+        const float t = s_t[j];
+        uint4 o;
+        if (mag != 0x7Fu && fabsf(t) <= FLT_MAX) {
+            o = make_uint4(nv_dec2<0>(w[j], bscale, t), nv_dec2<1>(w[j], bscale, t),
+                           nv_dec2<2>(w[j], bscale, t), nv_dec2<3>(w[j], bscale, t));
         } else {
-            o[0] = nv_dec2_nan<0>(w[j].x, bscale, st); o[1] = nv_dec2_nan<1>(w[j].x, bscale, st);
-            o[2] = nv_dec2_nan<2>(w[j].x, bscale, st); o[3] = nv_dec2_nan<3>(w[j].x, bscale, st);
-            o[4] = nv_dec2_nan<0>(w[j].y, bscale, st); o[5] = nv_dec2_nan<1>(w[j].y, bscale, st);
-            o[6] = nv_dec2_nan<2>(w[j].y, bscale, st); o[7] = nv_dec2_nan<3>(w[j].y, bscale, st);
+            o = make_uint4(nv_dec2_nan<0>(w[j], bscale, t), nv_dec2_nan<1>(w[j], bscale, t),
+                           nv_dec2_nan<2>(w[j], bscale, t), nv_dec2_nan<3>(w[j], bscale, t));
         }
-        if (b < n_blocks) {
-            y[2 * b] = make_uint4(o[0], o[1], o[2], o[3]);
-            y[2 * b + 1] = make_uint4(o[4], o[5], o[6], o[7]);
-        }
+        if (h < n_half) y[h] = o;
     }
 }
 
@@ -277,14 +289,21 @@ hipError_t launch_nv_quant(const void* x, int64_t R, int64_t K, void* q, void* s
 
 hipError_t launch_nv_dequant(const void* q, const void* sb, const float* st, int64_t R, int64_t K,
                              void* y, hipStream_t stream) {
-    const int64_t n_blocks = R * (K / 16);
-    const int64_t bpr = K / 16;
-    const int64_t tiles = (n_blocks + 64 * NVDQ_SLOTS - 1) / (64 * NVDQ_SLOTS);
-    const int64_t grid = (tiles + NVDQ_WAVES - 1) / NVDQ_WAVES;
-    hipLaunchKernelGGL(nv_dequant_kernel, dim3((unsigned)grid), dim3(64 * NVDQ_WAVES), 0, stream,
-                       (const uint2*)q, (const uint8_t*)sb, st, (uint4*)y, n_blocks, bpr,
-                       1.0 / (double)bpr);
-    return hipGetLastError();
+    // 32-bit half-block indices: launch row ranges of fewer than 2^31 half blocks each
+    const int64_t hpr = K / 8;
+    const int64_t rows_per_launch = ((int64_t)1 << 31) / hpr;
+    const FastDiv div = make_fastdiv((uint32_t)hpr);
+    for (int64_t r0 = 0; r0 < R; r0 += rows_per_launch) {
+        const int64_t rows = (R - r0 < rows_per_launch) ? R - r0 : rows_per_launch;
+        const int64_t n_half = rows * hpr;
+        const int64_t grid = (n_half + 256 * NVDQ_SLOTS - 1) / (256 * NVDQ_SLOTS);
+        hipLaunchKernelGGL(nv_dequant_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                           (const uint32_t*)q + r0 * hpr, (const uint8_t*)sb + r0 * (K / 16),
+                           st + r0, (uint4*)y + r0 * hpr, (uint32_t)n_half, div);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace bsq
