@@ -101,47 +101,69 @@ void mx_quant_rowwise_kernel(const uint4* __restrict__ x, uint2* __restrict__ q,
 //  * the columnwise copy q_col[K][M] is written as one 16-byte store per lane and
 //    column (16 rows of E4M3), so 8 lanes g = 0..7 fill 128 contiguous bytes of one
 //    q_col row: the transpose happens in registers and the writes stay coalesced.
-// Four waves of a workgroup take four neighbouring 64-column tiles of the same 128 rows,
-// so the rowwise q/s lines they share are completed inside one CU's L2.  Workgroups are
-// renumbered so that each XCD (workgroups are dealt round-robin over the 8 XCDs) gets a
-// contiguous range of row stripes.
+// A workgroup is WR x WC waves: WR wave tiles stacked down the rows and WC side by side
+// along the columns, so one workgroup covers (128 WR) x (64 WC) and its q_row lines are
+// 64 WC bytes and its q_col lines 128 WR bytes long.  Scale codes are gathered in LDS and
+// leave as one store per row / column of the workgroup tile.  Workgroups are renumbered
+// so that each XCD (workgroups are dealt round-robin over the 8 XCDs) gets a contiguous
+// range of row stripes.
 constexpr int TILE_ROWS = 128;
 constexpr int TILE_COLS = 64;
-constexpr int TILE_WAVES = 4;
 
-template <bool ROW>
-__global__ __launch_bounds__(64 * TILE_WAVES) __attribute__((amdgpu_waves_per_eu(4)))
-void mx_quant_tile_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
-                          uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
-                          uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
-                          int64_t col_groups, int64_t n_wg) {
-    // Scale codes of the workgroup tile (128 rows x 256 columns), gathered so they leave
-    // as one 8-byte store per row (rowwise scales) and one 4-byte store per column
-    // (columnwise scales) instead of one byte store per block.
-    __shared__ __align__(16) uint8_t lds_srow[TILE_ROWS][2 * TILE_WAVES];
-    __shared__ __align__(16) uint8_t lds_scol[TILE_WAVES * TILE_COLS][TILE_ROWS / 32];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int g = lane >> 3;
-    const int c = lane & 7;
+template <int N>
+__device__ __forceinline__ void store_bytes(uint8_t* dst, const uint8_t* src, int n, bool aligned) {
+    if (n == N && aligned) {
+        if constexpr (N == 16) *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+        else if constexpr (N == 8) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+        else if constexpr (N == 4) *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
+        else if constexpr (N == 2) *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(src);
+        else dst[0] = src[0];
+    } else {
+        for (int i = 0; i < n; ++i) dst[i] = src[i];
+    }
+}
 
-    int64_t w = blockIdx.x;
-    if ((n_wg & 7) == 0) w = (w & 7) * (n_wg >> 3) + (w >> 3);   // XCD-contiguous ranges
-    const int64_t r0 = (w / col_groups) * TILE_ROWS;
-    const int64_t kw = (w % col_groups) * (TILE_WAVES * TILE_COLS);  // workgroup's first column
-    const int64_t k0 = kw + wave * TILE_COLS;
+// Tile geometry of workgroup tile w (w in [0, n_wg)): first row and first column.
+//   ORDER 0: each XCD (workgroups are dealt round-robin over the 8 XCDs) a contiguous
+//            range of tile ids, row stripe major (columns fastest)
+//   ORDER 1: plain ids, row stripe major
+template <int ORDER>
+__device__ __forceinline__ void tile_origin(int64_t w, int64_t n_wg, int64_t col_groups,
+                                            int wg_rows, int wg_cols, int64_t& rw, int64_t& kw) {
+    if (ORDER == 0 && (n_wg & 7) == 0) w = (w & 7) * (n_wg >> 3) + (w >> 3);
+    rw = (w / col_groups) * wg_rows;
+    kw = (w % col_groups) * wg_cols;
+}
 
-    const int64_t row0 = r0 + 16 * g;          // first of this lane's 16 rows
-    const int64_t col0 = k0 + 8 * c;           // first of this lane's 8 columns
-    const bool rows_ok = row0 < M;             // M % 32 == 0: lane pairs agree
-    const bool cols_ok = col0 < K;             // K % 32 == 0: quads agree
-    const bool ok = rows_ok && cols_ok;
-
-    uint4 v[16];
+// Load the lane's 16 rows x 8 columns of the wave tile (zeros outside the tensor).
+__device__ __forceinline__ void load_tile(uint4 (&v)[16], const uint16_t* __restrict__ x,
+                                          int64_t K, int64_t row0, int64_t col0, bool ok) {
     const uint16_t* src = x + row0 * K + col0;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
         v[i] = ok ? *reinterpret_cast<const uint4*>(src + (int64_t)i * K) : make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Everything after the load for one workgroup tile: both copies' codes and stores, the
+// scale gather in LDS and the scale stores.  Called by every thread of the workgroup.
+template <bool ROW, int WR, int WC>
+__device__ __forceinline__ void process_tile(uint4 (&v)[16], int64_t M, int64_t K, int64_t rw, int64_t kw,
+                                             uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
+                                             uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
+                                             uint8_t (*lds_srow)[TILE_COLS * WC / 32],
+                                             uint8_t (*lds_scol)[TILE_ROWS * WR / 32]) {
+    constexpr int WG_ROWS = TILE_ROWS * WR, WG_COLS = TILE_COLS * WC;
+    constexpr int SROW_B = WG_COLS / 32, SCOL_B = WG_ROWS / 32;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wr = wave / WC, wc = wave % WC;
+    const int g = lane >> 3;
+    const int c = lane & 7;
+    const int64_t row0 = rw + wr * TILE_ROWS + 16 * g;
+    const int64_t col0 = kw + wc * TILE_COLS + 8 * c;
+    const bool ok = row0 < M && col0 < K;      // M, K % 32 == 0: lane pairs / quads agree
+    const int lrow = wr * TILE_ROWS + 16 * g;  // lane's first row inside the workgroup tile
+    const int lcol = wc * TILE_COLS + 8 * c;   // lane's first column inside the workgroup tile
 
     // ---- rowwise copy: each row of the lane, block = quad of lanes
     if (ROW) {
@@ -151,7 +173,7 @@ void mx_quant_tile_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
             const uint32_t code = e8m0_code_from_bf16_mag(amax);
             const uint2 out = mx_enc8(v[i], e8m0_decode(code));
             if (ok) *reinterpret_cast<uint2*>(q_row + (row0 + i) * K + col0) = out;
-            if ((c & 3) == 0) lds_srow[16 * g + i][2 * wave + (c >> 2)] = (uint8_t)code;
+            if ((c & 3) == 0) lds_srow[lrow + i][lcol >> 5] = (uint8_t)code;
         }
         // The column pass below re-derives its FP32 operands from the packed tile; this
         // empty register barrier stops the compiler from instead keeping the row pass's
@@ -201,38 +223,120 @@ void mx_quant_tile_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
             *reinterpret_cast<uint4*>(q_col + (ka + 1) * M + row0) = make_uint4(b[0], b[1], b[2], b[3]);
         }
         if ((g & 1) == 0) {
-            lds_scol[wave * TILE_COLS + 8 * c + 2 * d][g >> 1] = (uint8_t)code0;
-            lds_scol[wave * TILE_COLS + 8 * c + 2 * d + 1][g >> 1] = (uint8_t)code1;
+            lds_scol[lcol + 2 * d][lrow >> 5] = (uint8_t)code0;
+            lds_scol[lcol + 2 * d + 1][lrow >> 5] = (uint8_t)code1;
         }
     }
 
     __syncthreads();
-    const int t = threadIdx.x;
-    // rowwise scales: thread t < 128 writes row r0 + t's 8 bytes (blocks kw/32 .. +7)
-    if (ROW && t < TILE_ROWS && r0 + t < M) {
+    // rowwise scales: one store of SROW_B bytes per row of the workgroup tile
+    if (ROW) {
         const int64_t nb_row = K >> 5;
         const int64_t b0 = kw >> 5;
-        const int nb = (int)min((int64_t)(2 * TILE_WAVES), nb_row - b0);
-        uint8_t* dst = s_row + (r0 + t) * nb_row + b0;
-        if (nb == 2 * TILE_WAVES && (nb_row & 7) == 0) {
-            *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(lds_srow[t]);
-        } else {
-            for (int i = 0; i < nb; ++i) dst[i] = lds_srow[t][i];
+        const int nb = (int)min((int64_t)SROW_B, nb_row - b0);
+        for (int t = threadIdx.x; t < WG_ROWS; t += 64 * WR * WC) {
+            if (rw + t < M)
+                store_bytes<SROW_B>(s_row + (rw + t) * nb_row + b0, lds_srow[t], nb,
+                                    (nb_row % SROW_B) == 0);
         }
     }
-    // columnwise scales: thread t writes column kw + t's 4 bytes (row blocks r0/32 .. +3)
-    if (kw + t < K) {
+    // columnwise scales: one store of SCOL_B bytes per column of the workgroup tile
+    {
         const int64_t nb_col = M >> 5;
-        const int64_t b0 = r0 >> 5;
-        const int nb = (int)min((int64_t)(TILE_ROWS / 32), nb_col - b0);
-        uint8_t* dst = s_col + (kw + t) * nb_col + b0;
-        if (nb == TILE_ROWS / 32 && (nb_col & 3) == 0) {
-            *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(lds_scol[t]);
-        } else {
-            for (int i = 0; i < nb; ++i) dst[i] = lds_scol[t][i];
+        const int64_t b0 = rw >> 5;
+        const int nb = (int)min((int64_t)SCOL_B, nb_col - b0);
+        for (int t = threadIdx.x; t < WG_COLS; t += 64 * WR * WC) {
+            if (kw + t < K)
+                store_bytes<SCOL_B>(s_col + (kw + t) * nb_col + b0, lds_scol[t], nb,
+                                    (nb_col % SCOL_B) == 0);
         }
+    }
+    __syncthreads();                           // LDS is reused by the next tile
+}
+
+// One workgroup tile per workgroup.
+template <bool ROW, int WR, int WC, int ORDER>
+__global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(4)))
+void mx_quant_tile_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                          uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
+                          uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
+                          int64_t col_groups, int64_t n_wg) {
+    __shared__ __align__(16) uint8_t lds_srow[TILE_ROWS * WR][TILE_COLS * WC / 32];
+    __shared__ __align__(16) uint8_t lds_scol[TILE_COLS * WC][TILE_ROWS * WR / 32];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int64_t rw, kw;
+    tile_origin<ORDER>(blockIdx.x, n_wg, col_groups, TILE_ROWS * WR, TILE_COLS * WC, rw, kw);
+    const int64_t row0 = rw + (wave / WC) * TILE_ROWS + 16 * (lane >> 3);
+    const int64_t col0 = kw + (wave % WC) * TILE_COLS + 8 * (lane & 7);
+    uint4 v[16];
+    load_tile(v, x, K, row0, col0, row0 < M && col0 < K);
+    process_tile<ROW, WR, WC>(v, M, K, rw, kw, q_row, s_row, q_col, s_col, lds_srow, lds_scol);
+}
+
+// Persistent variant: each workgroup walks tiles blockIdx.x, blockIdx.x + gridDim.x, ...
+// and issues the loads of its next tile before encoding the current one, so HBM reads
+// stay in flight while the codes are computed and stored.
+template <bool ROW, int WR, int WC, int ORDER>
+__global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(3)))
+void mx_quant_tile_persistent_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                     uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
+                                     uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
+                                     int64_t col_groups, int64_t n_wg) {
+    __shared__ __align__(16) uint8_t lds_srow[TILE_ROWS * WR][TILE_COLS * WC / 32];
+    __shared__ __align__(16) uint8_t lds_scol[TILE_COLS * WC][TILE_ROWS * WR / 32];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t lr = (wave / WC) * TILE_ROWS + 16 * (lane >> 3);
+    const int64_t lc = (wave % WC) * TILE_COLS + 8 * (lane & 7);
+    int64_t w = blockIdx.x;
+    if (w >= n_wg) return;                     // uniform over the workgroup
+    int64_t rw, kw;
+    tile_origin<ORDER>(w, n_wg, col_groups, TILE_ROWS * WR, TILE_COLS * WC, rw, kw);
+    uint4 v[16];
+    load_tile(v, x, K, rw + lr, kw + lc, rw + lr < M && kw + lc < K);
+    for (;;) {
+        const int64_t wn = w + gridDim.x;
+        int64_t rn = 0, kn = 0;
+        uint4 vn[16];
+        if (wn < n_wg) {
+            tile_origin<ORDER>(wn, n_wg, col_groups, TILE_ROWS * WR, TILE_COLS * WC, rn, kn);
+            load_tile(vn, x, K, rn + lr, kn + lc, rn + lr < M && kn + lc < K);
+        }
+        process_tile<ROW, WR, WC>(v, M, K, rw, kw, q_row, s_row, q_col, s_col, lds_srow, lds_scol);
+        if (wn >= n_wg) break;
+        w = wn;
+        rw = rn;
+        kw = kn;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = vn[i];
     }
 }
+
+template <bool ROW, int WR, int WC, int ORDER = 0>
+static void launch_tile(const void* x, int64_t M, int64_t K, void* q_row, void* s_row,
+                        void* q_col, void* s_col, hipStream_t stream, int64_t persistent_wgs = 0) {
+    const int64_t row_stripes = (M + TILE_ROWS * WR - 1) / (TILE_ROWS * WR);
+    const int64_t col_groups = (K + TILE_COLS * WC - 1) / (TILE_COLS * WC);
+    const int64_t n_wg = row_stripes * col_groups;
+    if (persistent_wgs > 0 && persistent_wgs < n_wg) {
+        hipLaunchKernelGGL((mx_quant_tile_persistent_kernel<ROW, WR, WC, ORDER>), dim3((unsigned)persistent_wgs),
+                           dim3(64 * WR * WC), 0, stream, (const uint16_t*)x, M, K, (uint8_t*)q_row,
+                           (uint8_t*)s_row, (uint8_t*)q_col, (uint8_t*)s_col, col_groups, n_wg);
+    } else {
+        hipLaunchKernelGGL((mx_quant_tile_kernel<ROW, WR, WC, ORDER>), dim3((unsigned)n_wg), dim3(64 * WR * WC),
+                           0, stream, (const uint16_t*)x, M, K, (uint8_t*)q_row, (uint8_t*)s_row,
+                           (uint8_t*)q_col, (uint8_t*)s_col, col_groups, n_wg);
+    }
+}
+
+// Workgroup arrangement used by the library (wave tiles down x across), and the number of
+// persistent workgroups (one per compute unit of an MI355X) used once a tensor has more
+// tiles than that many workgroups can hold twice over.  Measured on the 65536 x 2048
+// activations: 130 us with one tile per workgroup, 114 us persistent with 256 workgroups
+// walking the tiles in row-stripe order (the tiles in flight then form one contiguous
+// band, so concurrent reads and the concurrent q_col writes of each k-row are contiguous).
+constexpr int TILE_WR = 1;
+constexpr int TILE_WC = 4;
+constexpr int TILE_PERSISTENT_WGS = 256;
 
 // ----------------------------------------------------------------------------- dequant
 
@@ -240,7 +344,7 @@ void mx_quant_tile_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
 // a workgroup owns, in slot j, the 8 codes of chunk blockIdx*256*DQ_SLOTS + 256 j + t and
 // writes their 16 bytes of BF16, so every load instruction reads 512 contiguous bytes
 // and every store instruction writes 1 KiB contiguous; 4 neighbouring lanes share a scale.
-constexpr int DQ_SLOTS = 2;
+constexpr int MX_DQ_SLOTS = 2;
 
 __device__ __forceinline__ uint32_t fix_nan_pair(uint32_t y, uint32_t codes2) {
     const uint32_t lo = ((codes2 & 0x7Fu) == 0x7Fu) ? 0x7FC0u : (y & 0xFFFFu);
@@ -270,6 +374,7 @@ __device__ __forceinline__ uint4 mx_dec8(uint32_t w0, uint32_t w1, uint32_t c) {
     return o;
 }
 
+template <int DQ_SLOTS>
 __global__ __launch_bounds__(256)
 void mx_dequant_kernel(const uint2* __restrict__ q, const uint8_t* __restrict__ s,
                        uint4* __restrict__ y, int64_t n_chunks) {
@@ -304,27 +409,28 @@ hipError_t launch_mx_quant(const void* x, int64_t M, int64_t K, int mode,
                            stream, (const uint4*)x, (uint2*)q_row, (uint8_t*)s_row, n_chunks);
         return hipGetLastError();
     }
-    const int64_t row_stripes = (M + TILE_ROWS - 1) / TILE_ROWS;
-    const int64_t col_groups = (K + TILE_COLS * TILE_WAVES - 1) / (TILE_COLS * TILE_WAVES);
-    const int64_t n_wg = row_stripes * col_groups;
-    if (mode == 3) {
-        hipLaunchKernelGGL(mx_quant_tile_kernel<true>, dim3((unsigned)n_wg), dim3(64 * TILE_WAVES), 0,
-                           stream, (const uint16_t*)x, M, K, (uint8_t*)q_row, (uint8_t*)s_row,
-                           (uint8_t*)q_col, (uint8_t*)s_col, col_groups, n_wg);
-    } else {
-        hipLaunchKernelGGL(mx_quant_tile_kernel<false>, dim3((unsigned)n_wg), dim3(64 * TILE_WAVES), 0,
-                           stream, (const uint16_t*)x, M, K, (uint8_t*)nullptr, (uint8_t*)nullptr,
-                           (uint8_t*)q_col, (uint8_t*)s_col, col_groups, n_wg);
-    }
+    const int64_t n_wg = ((M + TILE_ROWS * TILE_WR - 1) / (TILE_ROWS * TILE_WR)) *
+                         ((K + TILE_COLS * TILE_WC - 1) / (TILE_COLS * TILE_WC));
+    const int64_t pw = (n_wg > 2 * TILE_PERSISTENT_WGS) ? TILE_PERSISTENT_WGS : 0;
+    if (mode == 3)
+        launch_tile<true, TILE_WR, TILE_WC, 1>(x, M, K, q_row, s_row, q_col, s_col, stream, pw);
+    else
+        launch_tile<false, TILE_WR, TILE_WC, 1>(x, M, K, nullptr, nullptr, q_col, s_col, stream, pw);
     return hipGetLastError();
+}
+
+template <int SLOTS>
+static void launch_mx_dequant_slots(const void* q, const void* s, int64_t rows, int64_t cols,
+                                    void* y, hipStream_t stream) {
+    const int64_t n_chunks = rows * cols / 8;
+    const int64_t grid = (n_chunks + 256 * SLOTS - 1) / (256 * SLOTS);
+    hipLaunchKernelGGL(mx_dequant_kernel<SLOTS>, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const uint2*)q, (const uint8_t*)s, (uint4*)y, n_chunks);
 }
 
 hipError_t launch_mx_dequant(const void* q, const void* s, int64_t rows, int64_t cols,
                              void* y, hipStream_t stream) {
-    const int64_t n_chunks = rows * cols / 8;
-    const int64_t grid = (n_chunks + 256 * DQ_SLOTS - 1) / (256 * DQ_SLOTS);
-    hipLaunchKernelGGL(mx_dequant_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                       (const uint2*)q, (const uint8_t*)s, (uint4*)y, n_chunks);
+    launch_mx_dequant_slots<MX_DQ_SLOTS>(q, s, rows, cols, y, stream);
     return hipGetLastError();
 }
 

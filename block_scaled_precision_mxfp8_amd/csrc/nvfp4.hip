@@ -78,28 +78,24 @@ void nv_check_offsets_kernel(const int64_t* __restrict__ off, int64_t E, int64_t
 constexpr int NV_WAVES = 4;
 
 template <int NS>
-__global__ __launch_bounds__(64 * NV_WAVES)
-void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
-                          uint8_t* __restrict__ sb, float* __restrict__ st,
-                          int64_t R, int64_t K,
-                          const int64_t* __restrict__ offsets, int64_t E,
-                          int32_t* __restrict__ status) {
+__device__ __forceinline__ void load_row(uint4 (&v)[NS], const uint4* __restrict__ xr, int64_t cpr) {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    if (status != nullptr && blockIdx.x == 0 && wave == 0) check_offsets(offsets, E, R, status);
-    const int64_t row = (int64_t)blockIdx.x * NV_WAVES + wave;
-    if (row >= R) return;
-
-    const int64_t cpr = K >> 3;                       // 8-element chunks per row
-    const uint4* xr = x + row * cpr;
-    uint4 v[NS];
-    uint32_t m = 0u;
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
         const int64_t ch = 64 * j + lane;
         v[j] = (ch < cpr) ? xr[ch] : make_uint4(0u, 0u, 0u, 0u);
-        m = max(m, chunk_absmax8(v[j]));
     }
+}
+
+// Quantize one row held in v (all lanes of the wave take part).
+template <int NS>
+__device__ __forceinline__ void quant_row(const uint4 (&v)[NS], int64_t row, int64_t K, int64_t cpr,
+                                          uint32_t* __restrict__ q, uint8_t* __restrict__ sb,
+                                          float* __restrict__ st) {
+    const int lane = threadIdx.x & 63;
+    uint32_t m = 0u;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) m = max(m, chunk_absmax8(v[j]));
     const uint32_t amax_t = group_max<64>(m);
     const float s_t = __uint_as_float(amax_t << 16) / 2688.0f;     // fl(amax / (6 * 448))
     const float p = 6.0f * s_t;                                     // fl(6 s_t)
@@ -144,6 +140,54 @@ void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
         }
     }
     if (lane == 0) st[row] = s_t;
+}
+
+// One row per wave.
+template <int NS>
+__global__ __launch_bounds__(64 * NV_WAVES)
+void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
+                          uint8_t* __restrict__ sb, float* __restrict__ st,
+                          int64_t R, int64_t K,
+                          const int64_t* __restrict__ offsets, int64_t E,
+                          int32_t* __restrict__ status) {
+    const int wave = threadIdx.x >> 6;
+    if (status != nullptr && blockIdx.x == 0 && wave == 0) check_offsets(offsets, E, R, status);
+    const int64_t row = (int64_t)blockIdx.x * NV_WAVES + wave;
+    if (row >= R) return;
+    const int64_t cpr = K >> 3;                       // 8-element chunks per row
+    uint4 v[NS];
+    load_row<NS>(v, x + row * cpr, cpr);
+    quant_row<NS>(v, row, K, cpr, q, sb, st);
+}
+
+// Persistent waves: wave w takes rows w, w + W, w + 2W, ... (W waves in the grid) and
+// loads its next row before quantizing the current one, so reads stay in flight while
+// the codes are computed and stored.
+template <int NS>
+__global__ __launch_bounds__(64 * NV_WAVES)
+void nv_quant_rows_persistent_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
+                                     uint8_t* __restrict__ sb, float* __restrict__ st,
+                                     int64_t R, int64_t K,
+                                     const int64_t* __restrict__ offsets, int64_t E,
+                                     int32_t* __restrict__ status) {
+    const int wave = threadIdx.x >> 6;
+    if (status != nullptr && blockIdx.x == 0 && wave == 0) check_offsets(offsets, E, R, status);
+    const int64_t stride = (int64_t)gridDim.x * NV_WAVES;
+    int64_t row = (int64_t)blockIdx.x * NV_WAVES + wave;
+    if (row >= R) return;
+    const int64_t cpr = K >> 3;
+    uint4 v[NS];
+    load_row<NS>(v, x + row * cpr, cpr);
+    for (;;) {
+        const int64_t next = row + stride;
+        uint4 vn[NS];
+        if (next < R) load_row<NS>(vn, x + next * cpr, cpr);
+        quant_row<NS>(v, row, K, cpr, q, sb, st);
+        if (next >= R) break;
+        row = next;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) v[j] = vn[j];
+    }
 }
 
 // Rows longer than the register-resident variants: two passes over the row (the second
@@ -193,7 +237,7 @@ void nv_quant_rows_long_kernel(const uint4* __restrict__ x, uint32_t* __restrict
 // slot j, so loads read 256 contiguous bytes and stores write 1 KiB contiguous per
 // instruction.  The row of half block h is h / (K/8), an exact multiply-high division.
 // y = RNE_BF16(fl(exact(DEC_E2M1(q) DEC_E4M3(sb)) s_t)).
-constexpr int NVDQ_SLOTS = 2;
+constexpr int NV_DQ_SLOTS = 2;
 
 // Two BF16 (one dword) of the E2M1 codes in byte `sel` of `word`; the inner product is
 // exact, the product with s_t is one binary32 rounding, the convert is RNE to BF16.
@@ -215,6 +259,7 @@ __device__ __forceinline__ uint32_t nv_dec2_nan(uint32_t word, float bscale, flo
     return lo | hi;
 }
 
+template <int NVDQ_SLOTS>
 __global__ __launch_bounds__(256)
 void nv_dequant_kernel(const uint32_t* __restrict__ q, const uint8_t* __restrict__ sb,
                        const float* __restrict__ st, uint4* __restrict__ y,
@@ -252,12 +297,23 @@ void nv_dequant_kernel(const uint32_t* __restrict__ q, const uint8_t* __restrict
 
 // ----------------------------------------------------------------------------- launch
 
+// Persistent workgroups for long row lists (0 = one row per wave).
+constexpr int64_t NV_PERSISTENT_WGS = 0;
+
 template <int NS>
 static void launch_rows(const void* x, int64_t R, int64_t K, void* q, void* sb, float* st,
-                        const int64_t* off, int64_t E, int32_t* status, hipStream_t stream) {
+                        const int64_t* off, int64_t E, int32_t* status, hipStream_t stream,
+                        int64_t persistent_wgs = NV_PERSISTENT_WGS) {
     const int64_t grid = (R + NV_WAVES - 1) / NV_WAVES;
-    hipLaunchKernelGGL(nv_quant_rows_kernel<NS>, dim3((unsigned)grid), dim3(64 * NV_WAVES), 0, stream,
-                       (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, st, R, K, off, E, status);
+    if (persistent_wgs > 0 && grid > 2 * persistent_wgs) {
+        hipLaunchKernelGGL(nv_quant_rows_persistent_kernel<NS>, dim3((unsigned)persistent_wgs),
+                           dim3(64 * NV_WAVES), 0, stream, (const uint4*)x, (uint32_t*)q,
+                           (uint8_t*)sb, st, R, K, off, E, status);
+    } else {
+        hipLaunchKernelGGL(nv_quant_rows_kernel<NS>, dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
+                           stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, st, R, K, off, E,
+                           status);
+    }
 }
 
 hipError_t launch_nv_quant(const void* x, int64_t R, int64_t K, void* q, void* sb, float* st,
@@ -287,8 +343,9 @@ hipError_t launch_nv_quant(const void* x, int64_t R, int64_t K, void* q, void* s
     return hipGetLastError();
 }
 
-hipError_t launch_nv_dequant(const void* q, const void* sb, const float* st, int64_t R, int64_t K,
-                             void* y, hipStream_t stream) {
+template <int SLOTS>
+static hipError_t launch_nv_dequant_slots(const void* q, const void* sb, const float* st, int64_t R,
+                                          int64_t K, void* y, hipStream_t stream) {
     // 32-bit half-block indices: launch row ranges of fewer than 2^31 half blocks each
     const int64_t hpr = K / 8;
     const int64_t rows_per_launch = ((int64_t)1 << 31) / hpr;
@@ -296,14 +353,19 @@ hipError_t launch_nv_dequant(const void* q, const void* sb, const float* st, int
     for (int64_t r0 = 0; r0 < R; r0 += rows_per_launch) {
         const int64_t rows = (R - r0 < rows_per_launch) ? R - r0 : rows_per_launch;
         const int64_t n_half = rows * hpr;
-        const int64_t grid = (n_half + 256 * NVDQ_SLOTS - 1) / (256 * NVDQ_SLOTS);
-        hipLaunchKernelGGL(nv_dequant_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+        const int64_t grid = (n_half + 256 * SLOTS - 1) / (256 * SLOTS);
+        hipLaunchKernelGGL(nv_dequant_kernel<SLOTS>, dim3((unsigned)grid), dim3(256), 0, stream,
                            (const uint32_t*)q + r0 * hpr, (const uint8_t*)sb + r0 * (K / 16),
                            st + r0, (uint4*)y + r0 * hpr, (uint32_t)n_half, div);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_nv_dequant(const void* q, const void* sb, const float* st, int64_t R, int64_t K,
+                             void* y, hipStream_t stream) {
+    return launch_nv_dequant_slots<NV_DQ_SLOTS>(q, sb, st, R, K, y, stream);
 }
 
 }  // namespace bsq
