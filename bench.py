@@ -51,6 +51,25 @@ def nv_bytes(R, K):             # BF16 <-> packed E2M1 + E4M3 per 16 + FP32 per 
     return 2 * R * K + R * K // 2 + R * K // 16 + 4 * R
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "nv_quant_grouped_524288x2048_traffic.json")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel, from the committed FETCH_SIZE/WRITE_SIZE
+    counter passes (scaled by the 1 GiB copy calibration), or None when the kernel's sources
+    have changed since the counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+        h = hashlib.sha256()
+        for p in rec["kernel_sources"]:
+            with open(os.path.join(ROOT, p), "rb") as fh:
+                h.update(fh.read())
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["kernel_sources_sha256"] else None
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
@@ -59,6 +78,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=1,
                    help="the CPU baseline runs 1/N of the step's rows")
+    p.add_argument("--all-configs", action="store_true",
+                   help="instead of the step: time every kernel of the five workloads on its own "
+                        "(512 MiB cache flush before each launch) and print one JSON line per op")
     p.add_argument("--profile-pass", action="store_true",
                    help="short run for hardware-counter passes: one 1 GiB device copy (the "
                         "counter calibration kernel), then the steps")
@@ -84,6 +106,8 @@ def main():
     bsq.lib()
 
     dev = torch.device("cuda:0")
+    if args.all_configs:
+        return all_configs(torch, bsq, workloads, dev)
     t_gen = time.time()
     cfg = workloads.config5()
     a_np, w_np, tok, off = cfg["a"], cfg["w"], cfg["token_idx"], cfg["offsets"]
@@ -181,7 +205,7 @@ def main():
         "elements_per_s": round(elems_step * args.steps / elapsed, 1),
         "roofline": {"bound": "hbm", "kernel": "nv_quant_rows_kernel<4> (grouped, 524288x2048)",
                      "achieved": round(nv_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(nv_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(nv_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": nv_launch_bytes,
                      "avg_launch_us": round(nv_avg_s * 1e6, 2)},
         "cpu_baseline": None,
@@ -192,6 +216,112 @@ def main():
         out["cpu_baseline"] = cpu_baseline(a_np, w_np, tok, args.cpu_sample)
 
     print(json.dumps(out), flush=True)
+
+
+def all_configs(torch, bsq, workloads, dev, reps=21):
+    """Median time of each op of each workload.  Before each launch a 512 MiB buffer is read
+    (a reduction, so the caches are left holding clean lines of that buffer): no input of
+    the timed op is served from the 256 MiB Infinity Cache or the L2, and no dirty lines of
+    the flush are written back while the op runs."""
+    flush = torch.ones(1 << 26, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def timed(fn):
+        ts = []
+        for i in range(reps):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+
+    def report(cfg, op, shape, nbytes, elems, fn):
+        us = timed(fn)
+        print(json.dumps({"config": cfg, "op": op, "shape": shape, "bytes": nbytes, "median_us": round(us, 2),
+                          "GB_s": round(nbytes / us / 1e3, 1), "pct_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS * 100, 1),
+                          "elems_per_s": round(elems / us * 1e6, 1)}), flush=True)
+
+    def mx_row(x):
+        M, K = x.shape
+        out = (torch.empty(M, K, dtype=torch.uint8, device=dev), torch.empty(M, K // 32, dtype=torch.uint8, device=dev))
+        return out, lambda: bsq.mx_quantize_mxfp8(x, "rowwise", out[0], out[1], stream=stream)
+
+    def mx_both(x):
+        M, K = x.shape
+        u8 = torch.uint8
+        out = (torch.empty(M, K, dtype=u8, device=dev), torch.empty(M, K // 32, dtype=u8, device=dev),
+               torch.empty(K, M, dtype=u8, device=dev), torch.empty(K, M // 32, dtype=u8, device=dev))
+        return out, lambda: bsq.mx_quantize_mxfp8(x, "both", *out, stream=stream)
+
+    def mx_dq(q, s):
+        y = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        return y, lambda: bsq.mx_dequantize(q, s, y, stream=stream)
+
+    def nv(x, off=None):
+        R, K = x.shape
+        out = (torch.empty(R, K // 2, dtype=torch.uint8, device=dev), torch.empty(R, K // 16, dtype=torch.uint8, device=dev),
+               torch.empty(R, dtype=torch.float32, device=dev))
+        if off is None:
+            return out, lambda: bsq.nv_quantize_nvfp4_per_token(x, *out, stream=stream)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        return out, lambda: bsq.nv_quantize_nvfp4_per_token_grouped(x, off, *out, status, stream=stream)
+
+    def nv_dq(q, sb, st):
+        y = torch.empty(q.shape[0], 2 * q.shape[1], dtype=torch.bfloat16, device=dev)
+        return y, lambda: bsq.nv_dequantize(q, sb, st, y, stream=stream)
+
+    def run(cfg, name, x, kind, off=None):
+        M, K = x.shape
+        shape = "%dx%d" % (M, K)
+        if kind == "mx_row":
+            out, fn = mx_row(x)
+            report(cfg, "mxfp8 rowwise quant " + name, shape, mx_both_bytes(M, K) - (M * K + M * K // 32), M * K, fn)
+            fn()
+            y, fn = mx_dq(out[0], out[1])
+            report(cfg, "mxfp8 dequant " + name, shape, mx_dq_bytes(M, K), M * K, fn)
+        elif kind == "mx_both":
+            out, fn = mx_both(x)
+            report(cfg, "mxfp8 dual quant " + name, shape, mx_both_bytes(M, K), M * K, fn)
+            fn()
+            y, fn = mx_dq(out[0], out[1])
+            report(cfg, "mxfp8 dequant rowwise copy " + name, shape, mx_dq_bytes(M, K), M * K, fn)
+            y, fn = mx_dq(out[2], out[3])
+            report(cfg, "mxfp8 dequant columnwise copy " + name, "%dx%d" % (K, M), mx_dq_bytes(K, M), M * K, fn)
+        else:
+            out, fn = nv(x, off)
+            report(cfg, "nvfp4 per-token quant%s %s" % (" grouped" if off is not None else "", name), shape,
+                   nv_bytes(M, K), M * K, fn)
+            fn()
+            y, fn = nv_dq(*out)
+            report(cfg, "nvfp4 dequant " + name, shape, nv_bytes(M, K), M * K, fn)
+        torch.cuda.synchronize()
+
+    run(1, "x", bf(workloads.config1()["x"]), "mx_row")
+    run(2, "x", bf(workloads.config2()["x"]), "mx_both")
+    c3 = workloads.config3(materialize=False)
+    h = bf(c3["h"])
+    run(3, "routed rows", h.index_select(0, torch.from_numpy(c3["token_idx"]).to(dev)), "nv",
+        torch.from_numpy(c3["offsets"]).to(dev))
+    del h
+    c4 = workloads.config4()
+    for key in ("gate_up", "down"):
+        w = bf(c4[key])
+        run(4, key, w, "nv")
+        run(4, key, w, "mx_row")
+        del w
+    del c4
+    c5 = workloads.config5()
+    a, w = bf(c5["a"]), bf(c5["w"])
+    run(5, "activations", a, "mx_both")
+    run(5, "weights", w, "mx_both")
+    run(5, "routed rows", a.index_select(0, torch.from_numpy(c5["token_idx"]).to(dev)), "nv",
+        torch.from_numpy(c5["offsets"]).to(dev))
 
 
 def cpu_baseline(a_np, w_np, tok, frac):

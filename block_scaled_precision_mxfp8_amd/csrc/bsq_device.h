@@ -189,6 +189,20 @@ __device__ __forceinline__ uint32_t pair_max(uint32_t v) {
     return max(v, dpp_xor1(v));
 }
 
+// Max over the whole wave, returned uniform: quad max by DPP, then the half-row mirror
+// (lane i <-> 7-i) and the row mirror (lane i <-> 15-i) give every lane its 16-lane row's
+// max, and the four row results are read into scalars.
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+    v = quad_max(v);
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true));  // row_half_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true));  // row_mirror
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(a, b), max(c, d));
+}
+
 // Max over aligned groups of `width` lanes (power of two, <= 64) via lane shuffles.
 template <int width>
 __device__ __forceinline__ uint32_t group_max(uint32_t v) {

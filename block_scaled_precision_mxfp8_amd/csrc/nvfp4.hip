@@ -77,26 +77,35 @@ void nv_check_offsets_kernel(const int64_t* __restrict__ off, int64_t E, int64_t
 // block is the lane pair (2i, 2i+1).
 constexpr int NV_WAVES = 4;
 
-template <int NS>
-__device__ __forceinline__ void load_row(uint4 (&v)[NS], const uint4* __restrict__ xr, int64_t cpr) {
+// Wave index as a scalar: all address arithmetic of a row is then wave-uniform and the
+// per-lane part is a 32-bit offset.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// FULL: the row is exactly NS slots long (K == 512 NS), so no lane is ever out of range.
+template <int NS, bool FULL>
+__device__ __forceinline__ void load_row(uint4 (&v)[NS], const uint4* __restrict__ xr, int cpr) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-        const int64_t ch = 64 * j + lane;
-        v[j] = (ch < cpr) ? xr[ch] : make_uint4(0u, 0u, 0u, 0u);
+        const int ch = 64 * j + lane;
+        v[j] = (FULL || ch < cpr) ? xr[ch] : make_uint4(0u, 0u, 0u, 0u);
     }
 }
 
-// Quantize one row held in v (all lanes of the wave take part).
-template <int NS>
-__device__ __forceinline__ void quant_row(const uint4 (&v)[NS], int64_t row, int64_t K, int64_t cpr,
+// Quantize one row held in v (all lanes of the wave take part).  The row's block-scale
+// bytes are gathered in the wave's LDS slice `lsb` (32 NS bytes) and leave as 16-byte
+// stores when the row's scale run is 16-byte aligned.
+template <int NS, bool FULL>
+__device__ __forceinline__ void quant_row(const uint4 (&v)[NS], int64_t row, int64_t K, int cpr,
                                           uint32_t* __restrict__ q, uint8_t* __restrict__ sb,
-                                          float* __restrict__ st) {
+                                          float* __restrict__ st, uint8_t* lsb) {
     const int lane = threadIdx.x & 63;
     uint32_t m = 0u;
 #pragma unroll
     for (int j = 0; j < NS; ++j) m = max(m, chunk_absmax8(v[j]));
-    const uint32_t amax_t = group_max<64>(m);
+    const uint32_t amax_t = wave_max(m);
     const float s_t = __uint_as_float(amax_t << 16) / 2688.0f;     // fl(amax / (6 * 448))
     const float p = 6.0f * s_t;                                     // fl(6 s_t)
 
@@ -124,65 +133,77 @@ __device__ __forceinline__ void quant_row(const uint4 (&v)[NS], int64_t row, int
             code1 = odd ? code : oc;
             f1 = odd ? f : of;
         }
-        const int64_t ch0 = 64 * j + lane;
+        const int ch0 = 64 * j + lane;
         const uint32_t packed0 = nv_enc8(v[j], f0);
-        if (ch0 < cpr) {
-            qr[ch0] = packed0;
-            if (!odd) sbr[ch0 >> 1] = (uint8_t)code0;
-        }
+        if (FULL || ch0 < cpr) qr[ch0] = packed0;
+        if (!odd) lsb[32 * j + (lane >> 1)] = (uint8_t)code0;
         if (two) {
-            const int64_t ch1 = 64 * (j + 1) + lane;
+            const int ch1 = 64 * (j + 1) + lane;
             const uint32_t packed1 = nv_enc8(v[j + 1], f1);
-            if (ch1 < cpr) {
-                qr[ch1] = packed1;
-                if (!odd) sbr[ch1 >> 1] = (uint8_t)code1;
-            }
+            if (FULL || ch1 < cpr) qr[ch1] = packed1;
+            if (!odd) lsb[32 * (j + 1) + (lane >> 1)] = (uint8_t)code1;
         }
     }
     if (lane == 0) st[row] = s_t;
+    // the wave's LDS slice: written above by even lanes, read below by the first lanes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int nsb = cpr >> 1;                         // scale bytes of the row
+    if ((nsb & 15) == 0) {
+        if (lane < (nsb >> 4))
+            reinterpret_cast<uint4*>(sbr)[lane] = reinterpret_cast<const uint4*>(lsb)[lane];
+    } else {
+        for (int i = lane; i < nsb; i += 64) sbr[i] = lsb[i];
+    }
+    // the slice is rewritten by the wave's next row
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
 }
 
 // One row per wave.
-template <int NS>
+template <int NS, bool FULL>
 __global__ __launch_bounds__(64 * NV_WAVES)
 void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
                           uint8_t* __restrict__ sb, float* __restrict__ st,
                           int64_t R, int64_t K,
                           const int64_t* __restrict__ offsets, int64_t E,
                           int32_t* __restrict__ status) {
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     if (status != nullptr && blockIdx.x == 0 && wave == 0) check_offsets(offsets, E, R, status);
     const int64_t row = (int64_t)blockIdx.x * NV_WAVES + wave;
     if (row >= R) return;
-    const int64_t cpr = K >> 3;                       // 8-element chunks per row
+    __shared__ __align__(16) uint8_t lds_sb[NV_WAVES][32 * NS];
+    const int cpr = (int)(K >> 3);                    // 8-element chunks per row
     uint4 v[NS];
-    load_row<NS>(v, x + row * cpr, cpr);
-    quant_row<NS>(v, row, K, cpr, q, sb, st);
+    load_row<NS, FULL>(v, x + row * cpr, cpr);
+    quant_row<NS, FULL>(v, row, K, cpr, q, sb, st, lds_sb[wave]);
 }
 
 // Persistent waves: wave w takes rows w, w + W, w + 2W, ... (W waves in the grid) and
 // loads its next row before quantizing the current one, so reads stay in flight while
 // the codes are computed and stored.
-template <int NS>
+template <int NS, bool FULL>
 __global__ __launch_bounds__(64 * NV_WAVES)
 void nv_quant_rows_persistent_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
                                      uint8_t* __restrict__ sb, float* __restrict__ st,
                                      int64_t R, int64_t K,
                                      const int64_t* __restrict__ offsets, int64_t E,
                                      int32_t* __restrict__ status) {
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     if (status != nullptr && blockIdx.x == 0 && wave == 0) check_offsets(offsets, E, R, status);
     const int64_t stride = (int64_t)gridDim.x * NV_WAVES;
     int64_t row = (int64_t)blockIdx.x * NV_WAVES + wave;
     if (row >= R) return;
-    const int64_t cpr = K >> 3;
+    __shared__ __align__(16) uint8_t lds_sb[NV_WAVES][32 * NS];
+    const int cpr = (int)(K >> 3);
     uint4 v[NS];
-    load_row<NS>(v, x + row * cpr, cpr);
+    load_row<NS, FULL>(v, x + row * cpr, cpr);
     for (;;) {
         const int64_t next = row + stride;
         uint4 vn[NS];
-        if (next < R) load_row<NS>(vn, x + next * cpr, cpr);
-        quant_row<NS>(v, row, K, cpr, q, sb, st);
+        if (next < R) load_row<NS, FULL>(vn, x + next * cpr, cpr);
+        quant_row<NS, FULL>(v, row, K, cpr, q, sb, st, lds_sb[wave]);
         if (next >= R) break;
         row = next;
 #pragma unroll
@@ -210,7 +231,7 @@ void nv_quant_rows_long_kernel(const uint4* __restrict__ x, uint32_t* __restrict
         const int64_t ch = base + lane;
         if (ch < cpr) m = max(m, chunk_absmax8(xr[ch]));
     }
-    const uint32_t amax_t = group_max<64>(m);
+    const uint32_t amax_t = wave_max(m);
     const float s_t = __uint_as_float(amax_t << 16) / 2688.0f;
     const float p = 6.0f * s_t;
     uint32_t* qr = q + row * cpr;
@@ -300,20 +321,30 @@ void nv_dequant_kernel(const uint32_t* __restrict__ q, const uint8_t* __restrict
 // Persistent workgroups for long row lists (0 = one row per wave).
 constexpr int64_t NV_PERSISTENT_WGS = 0;
 
+template <int NS, bool FULL>
+static void launch_rows_full(const void* x, int64_t R, int64_t K, void* q, void* sb, float* st,
+                             const int64_t* off, int64_t E, int32_t* status, hipStream_t stream,
+                             int64_t persistent_wgs) {
+    const int64_t grid = (R + NV_WAVES - 1) / NV_WAVES;
+    if (persistent_wgs > 0 && grid > 2 * persistent_wgs) {
+        hipLaunchKernelGGL((nv_quant_rows_persistent_kernel<NS, FULL>), dim3((unsigned)persistent_wgs),
+                           dim3(64 * NV_WAVES), 0, stream, (const uint4*)x, (uint32_t*)q,
+                           (uint8_t*)sb, st, R, K, off, E, status);
+    } else {
+        hipLaunchKernelGGL((nv_quant_rows_kernel<NS, FULL>), dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
+                           stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, st, R, K, off, E,
+                           status);
+    }
+}
+
 template <int NS>
 static void launch_rows(const void* x, int64_t R, int64_t K, void* q, void* sb, float* st,
                         const int64_t* off, int64_t E, int32_t* status, hipStream_t stream,
                         int64_t persistent_wgs = NV_PERSISTENT_WGS) {
-    const int64_t grid = (R + NV_WAVES - 1) / NV_WAVES;
-    if (persistent_wgs > 0 && grid > 2 * persistent_wgs) {
-        hipLaunchKernelGGL(nv_quant_rows_persistent_kernel<NS>, dim3((unsigned)persistent_wgs),
-                           dim3(64 * NV_WAVES), 0, stream, (const uint4*)x, (uint32_t*)q,
-                           (uint8_t*)sb, st, R, K, off, E, status);
-    } else {
-        hipLaunchKernelGGL(nv_quant_rows_kernel<NS>, dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
-                           stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, st, R, K, off, E,
-                           status);
-    }
+    if (K == 512 * NS)
+        launch_rows_full<NS, true>(x, R, K, q, sb, st, off, E, status, stream, persistent_wgs);
+    else
+        launch_rows_full<NS, false>(x, R, K, q, sb, st, off, E, status, stream, persistent_wgs);
 }
 
 hipError_t launch_nv_quant(const void* x, int64_t R, int64_t K, void* q, void* sb, float* st,
