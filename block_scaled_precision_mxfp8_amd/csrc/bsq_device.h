@@ -165,6 +165,51 @@ __device__ __forceinline__ uint32_t fastdiv(uint32_t n, const FastDiv& f) {
     return (uint32_t)(t >> 32);
 }
 
+// ----------------------------------------------------------------------------- streaming access
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Loads of inputs and stores of outputs that a kernel touches exactly once.  NT selects
+// the non-temporal form (the caches do not keep the line for reuse); each kernel family
+// picks its policy from measurements.
+template <bool NT>
+__device__ __forceinline__ void st_stream(uint32_t* p, uint32_t v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p); else *p = v;
+}
+template <bool NT>
+__device__ __forceinline__ void st_stream(uint2* p, uint2 v) {
+    if constexpr (NT) __builtin_nontemporal_store(u32x2_t{v.x, v.y}, reinterpret_cast<u32x2_t*>(p));
+    else *p = v;
+}
+template <bool NT>
+__device__ __forceinline__ void st_stream(uint4* p, uint4 v) {
+    if constexpr (NT)
+        __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+    else *p = v;
+}
+template <bool NT>
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+    if constexpr (NT) {
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    }
+    return *p;
+}
+template <bool NT>
+__device__ __forceinline__ uint2 ld_stream(const uint2* p) {
+    if constexpr (NT) {
+        const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+        return make_uint2(v.x, v.y);
+    }
+    return *p;
+}
+template <bool NT>
+__device__ __forceinline__ uint32_t ld_stream(const uint32_t* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    return *p;
+}
+
 // ----------------------------------------------------------------------------- lanes
 
 // DPP quad permutations: value of the lane (i ^ 1) and (i ^ 2) within each quad.
