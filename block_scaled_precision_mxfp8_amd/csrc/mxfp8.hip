@@ -110,218 +110,312 @@ void mx_quant_rowwise_kernel(const uint4* __restrict__ x, uint2* __restrict__ q,
 
 // ----------------------------------------------------------------------------- col / both
 
-// Columnwise (and dual) quantization of x[M][K].  One wave owns a 128-row x 64-column
-// tile.  Lane l = 8*g + c holds rows 16*g .. 16*g+15 of the tile and columns 8*c .. 8*c+7
-// (one 16-byte chunk per row, 16 chunks = 64 VGPRs):
+// Columnwise (and dual) quantization of x[M][K] (M % 32 == 0, K % 32 == 0).  One wave
+// owns a 128-row x 64-column tile.  Lane l = 8*g + c holds rows 16*g .. 16*g+15 of the
+// tile and columns 8*c .. 8*c+7 (one 16-byte chunk per row, 16 chunks = 64 VGPRs):
 //  * a 32x1 column block is held by the lane pair (g, g^1) -- 16 rows each -- so its
-//    maximum is a lane-local packed max plus one lane exchange;
+//    maximum is a lane-local packed max plus one DPP exchange between lanes 8 apart;
 //  * a 1x32 row block is the quad of lanes c = 4k .. 4k+3 of one row (DPP);
 //  * every load instruction reads 8 rows x 128 bytes (full lines);
 //  * the columnwise copy q_col[K][M] is written as one 16-byte store per lane and
-//    column (16 rows of E4M3), so 8 lanes g = 0..7 fill 128 contiguous bytes of one
-//    q_col row: the transpose happens in registers and the writes stay coalesced.
-// A workgroup is WR x WC waves: WR wave tiles stacked down the rows and WC side by side
-// along the columns, so one workgroup covers (128 WR) x (64 WC) and its q_row lines are
-// 64 WC bytes and its q_col lines 128 WR bytes long.  Scale codes are gathered in LDS and
-// leave as one store per row / column of the workgroup tile.  Workgroups are renumbered
-// so that each XCD (workgroups are dealt round-robin over the 8 XCDs) gets a contiguous
-// range of row stripes.
+//    column (16 rows of E4M3), so the 8 lanes g = 0..7 fill 128 contiguous bytes of one
+//    q_col row: the transpose happens in registers and the writes stay coalesced;
+//  * the rowwise codes of the whole workgroup tile are staged in LDS and leave as
+//    16-byte stores covering whole rows of the tile, so no store writes part of a line.
+// A workgroup is WR x WC wave tiles (TileGeom).  Scale codes are gathered in LDS and
+// leave as one store per row / column of the workgroup tile.
+//
+// Addressing: every pointer is a uniform (scalar) tile base plus a per-lane byte offset
+// that does not change from tile to tile.  When all offsets inside a workgroup tile fit
+// in 31 bits (OffT = uint32_t) the loads and stores take the scalar-base + 32-bit-offset
+// form and no per-access vector address arithmetic is left; larger tensors use 64-bit
+// offsets.  FULL (M and K multiples of the workgroup tile) drops every bounds mask.  In
+// ragged tiles lanes outside the tensor load the tile origin instead (always inside the
+// tensor, since M - row0 >= 32 for a tile that starts inside it) and skip their stores;
+// because M and K are multiples of 32, a row quad or column pair never mixes lanes inside
+// and outside the tensor.
 constexpr int TILE_ROWS = 128;
 constexpr int TILE_COLS = 64;
 
+// N scale bytes (N = 2, 4, 8 or 16) from LDS to an N-aligned global address.
 template <int N>
-__device__ __forceinline__ void store_bytes(uint8_t* dst, const uint8_t* src, int n, bool aligned) {
-    if (n == N && aligned) {
-        if constexpr (N == 16) *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-        else if constexpr (N == 8) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
-        else if constexpr (N == 4) *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
-        else if constexpr (N == 2) *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(src);
-        else dst[0] = src[0];
+__device__ __forceinline__ void store_scales(uint8_t* dst, const uint8_t* src) {
+    if constexpr (N == 16) *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+    else if constexpr (N == 8) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+    else if constexpr (N == 4) *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
+    else *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(src);
+}
+
+// Workgroup geometry: WR x WC wave tiles (WR down the rows, WC along the columns).
+template <int WR_, int WC_>
+struct TileGeom {
+    static constexpr int WR = WR_, WC = WC_;
+    static constexpr int ROWS = TILE_ROWS * WR;     // workgroup tile rows
+    static constexpr int COLS = TILE_COLS * WC;     // workgroup tile columns
+    static constexpr int SROW_B = COLS / 32;        // row-scale bytes per row of the tile
+    static constexpr int SCOL_B = ROWS / 32;        // column-scale bytes per column
+    static constexpr int THREADS = 64 * WR * WC;
+    static constexpr int QPITCH = COLS + 16;        // LDS row pitch of the staged q_row tile
+};
+
+// E8M0 code of a block from its maximum magnitude (BF16 bits, finite): E - 8 + [m > 0x60]
+// clamped at 0, computed as (max(a - 0x3E1, 0)) >> 7 -- adding 0x1F carries into the
+// exponent field exactly when the mantissa exceeds 0x60, and 0x400 = 8 << 7.
+__device__ __forceinline__ uint32_t mx_code(uint32_t amax) {
+    return __builtin_elementwise_sub_sat(amax, 0x3E1u) >> 7;
+}
+// Same for the high half of a packed pair (the low half only affects bits below 16).
+__device__ __forceinline__ uint32_t mx_code_hi(uint32_t pair) {
+    return __builtin_elementwise_sub_sat(pair, 0x3E1u << 16) >> 23;
+}
+// The scale operand of the scaled convert: the binary32 value 2^(c-127) (2^-127 is the
+// subnormal 0x00400000, which the convert reads as exponent -127).
+__device__ __forceinline__ float mx_scale(uint32_t c) {
+    return __builtin_amdgcn_ldexpf(__uint_as_float(0x00400000u), (int)c);
+}
+
+__device__ __forceinline__ uint32_t pk_absmax(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+// Both halves of a packed magnitude pair replaced by the larger one (one packed max with
+// swapped halves); the result orders like the maximum itself under unsigned compares.
+__device__ __forceinline__ uint32_t pk_fold(uint32_t m) {
+    const u16x2 a = __builtin_bit_cast(u16x2, m);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, a.yx));
+}
+
+// Four E4M3 codes of the BF16 pairs w0 (bytes 0-1) and w1 (bytes 2-3) at one block scale.
+// The convert writes half of its destination; `spare` is any value that is dead after
+// the call, handed over as that destination so that no register has to be cleared.
+__device__ __forceinline__ uint32_t cvt_e4m3x4_into(uint32_t spare, uint32_t w0, uint32_t w1, float scale) {
+    short2_t r = __builtin_bit_cast(short2_t, spare);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2_t, w0), scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2_t, w1), scale, true);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Workgroup tile w -> first row and first column.
+//   ORDER 0: row stripes in order, column groups fastest (the tiles in flight form one
+//            band of full rows: contiguous reads and q_row writes)
+//   ORDER 1: column groups in order, row stripes fastest (the tiles in flight form one
+//            band of full columns: contiguous q_col writes)
+template <class G, int ORDER>
+__device__ __forceinline__ void tile_origin(int64_t w, int64_t row_stripes, int64_t col_groups,
+                                            int64_t& rw, int64_t& kw) {
+    if (ORDER == 0) {
+        const int64_t s = w / col_groups;
+        rw = s * G::ROWS;
+        kw = (w - s * col_groups) * G::COLS;
     } else {
-        for (int i = 0; i < n; ++i) dst[i] = src[i];
+        const int64_t g = w / row_stripes;
+        kw = g * G::COLS;
+        rw = (w - g * row_stripes) * G::ROWS;
     }
 }
 
-// Tile geometry of workgroup tile w (w in [0, n_wg)): first row and first column.
-//   ORDER 0: each XCD (workgroups are dealt round-robin over the 8 XCDs) a contiguous
-//            range of tile ids, row stripe major (columns fastest)
-//   ORDER 1: plain ids, row stripe major
-template <int ORDER>
-__device__ __forceinline__ void tile_origin(int64_t w, int64_t n_wg, int64_t col_groups,
-                                            int wg_rows, int wg_cols, int64_t& rw, int64_t& kw) {
-    if (ORDER == 0 && (n_wg & 7) == 0) w = (w & 7) * (n_wg >> 3) + (w >> 3);
-    rw = (w / col_groups) * wg_rows;
-    kw = (w % col_groups) * wg_cols;
+// Per-lane constants of the tile layout.
+template <typename OffT>
+struct TileLane {
+    int lrow, lcol;          // lane's first row / column inside the workgroup tile
+    OffT xo, co;             // byte offsets from the tile origin in x and q_col
+};
+
+template <class G, typename OffT>
+__device__ __forceinline__ TileLane<OffT> tile_lane(int64_t M, int64_t K) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    TileLane<OffT> t;
+    t.lrow = (wave / G::WC) * TILE_ROWS + 16 * (lane >> 3);
+    t.lcol = (wave % G::WC) * TILE_COLS + 8 * (lane & 7);
+    t.xo = (OffT)(2 * ((int64_t)t.lrow * K + t.lcol));
+    t.co = (OffT)((int64_t)t.lcol * M + t.lrow);
+    return t;
 }
 
-// Load the lane's 16 rows x 8 columns of the wave tile (zeros outside the tensor).
-__device__ __forceinline__ void load_tile(uint4 (&v)[16], const uint16_t* __restrict__ x,
-                                          int64_t K, int64_t row0, int64_t col0, bool ok) {
-    const uint16_t* src = x + row0 * K + col0;
+template <bool FULL, typename OffT>
+__device__ __forceinline__ void load_tile(uint4 (&v)[16], const uint16_t* __restrict__ x, int64_t M,
+                                          int64_t K, int64_t rw, int64_t kw, const TileLane<OffT>& t) {
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(x + rw * K + kw);
+    OffT o = t.xo;
+    if (!FULL && !(rw + t.lrow < M && kw + t.lcol < K)) o = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-        v[i] = ok ? ld_stream<MXTILE_NT_LOAD>(reinterpret_cast<const uint4*>(src + (int64_t)i * K)) : make_uint4(0u, 0u, 0u, 0u);
+        v[i] = ld_stream<MXTILE_NT_LOAD>(reinterpret_cast<const uint4*>(base + 2 * i * K + o));
 }
 
 // Everything after the load for one workgroup tile: both copies' codes and stores, the
 // scale gather in LDS and the scale stores.  Called by every thread of the workgroup.
-template <bool ROW, int WR, int WC>
+template <class G, bool ROW, bool FULL, typename OffT>
 __device__ __forceinline__ void process_tile(uint4 (&v)[16], int64_t M, int64_t K, int64_t rw, int64_t kw,
+                                             const TileLane<OffT>& t,
                                              uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
                                              uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
-                                             uint8_t (*lds_srow)[TILE_COLS * WC / 32],
-                                             uint8_t (*lds_scol)[TILE_ROWS * WR / 32]) {
-    constexpr int WG_ROWS = TILE_ROWS * WR, WG_COLS = TILE_COLS * WC;
-    constexpr int SROW_B = WG_COLS / 32, SCOL_B = WG_ROWS / 32;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wr = wave / WC, wc = wave % WC;
-    const int g = lane >> 3;
-    const int c = lane & 7;
-    const int64_t row0 = rw + wr * TILE_ROWS + 16 * g;
-    const int64_t col0 = kw + wc * TILE_COLS + 8 * c;
-    const bool ok = row0 < M && col0 < K;      // M, K % 32 == 0: lane pairs / quads agree
-    const int lrow = wr * TILE_ROWS + 16 * g;  // lane's first row inside the workgroup tile
-    const int lcol = wc * TILE_COLS + 8 * c;   // lane's first column inside the workgroup tile
+                                             uint8_t (*lds_srow)[G::SROW_B], uint8_t (*lds_scol)[G::SCOL_B],
+                                             uint8_t (*lds_q)[G::QPITCH]) {
+    const bool ok = FULL || (rw + t.lrow < M && kw + t.lcol < K);
+    uint8_t* qc = q_col + kw * M + rw;
 
-    // ---- rowwise copy: each row of the lane, block = quad of lanes
-    if (ROW) {
+    // ---- rowwise copy (each row of the lane; block = quad of lanes) and the packed
+    //      column maxima over the lane's 16 rows, from one set of magnitudes
+    uint32_t cm[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t amax = quad_max(chunk_absmax(v[i]));
-            const uint32_t code = e8m0_code_from_bf16_mag(amax);
-            const uint2 out = mx_enc8(v[i], e8m0_decode(code));
-            if (ok) st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint2*>(q_row + (row0 + i) * K + col0), out);
-            if ((c & 3) == 0) lds_srow[lrow + i][lcol >> 5] = (uint8_t)code;
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t a0 = v[i].x & 0x7FFF7FFFu, a1 = v[i].y & 0x7FFF7FFFu;
+        const uint32_t a2 = v[i].z & 0x7FFF7FFFu, a3 = v[i].w & 0x7FFF7FFFu;
+        cm[0] = pk_absmax(cm[0], a0);
+        cm[1] = pk_absmax(cm[1], a1);
+        cm[2] = pk_absmax(cm[2], a2);
+        cm[3] = pk_absmax(cm[3], a3);
+        if (ROW) {
+            const uint32_t m = pk_absmax(pk_absmax(a0, a1), pk_absmax(a2, a3));
+            const uint32_t code = mx_code_hi(quad_max(pk_fold(m)));
+            const float sc = mx_scale(code);
+            const uint2 out = make_uint2(cvt_e4m3x4_into(a0, v[i].x, v[i].y, sc),
+                                         cvt_e4m3x4_into(a2, v[i].z, v[i].w, sc));
+            *reinterpret_cast<uint2*>(&lds_q[t.lrow + i][t.lcol]) = out;
+            lds_srow[t.lrow + i][t.lcol >> 5] = (uint8_t)code;   // the quad writes one value
         }
-        // The column pass below re-derives its FP32 operands from the packed tile; this
-        // empty register barrier stops the compiler from instead keeping the row pass's
-        // unpacked values alive (which would double the live tile and spill).
+    }
+    if (ROW) {
+        // The column pass below re-reads the packed tile; this empty register barrier keeps
+        // the compiler from carrying row-pass temporaries into it instead.
 #pragma unroll
         for (int i = 0; i < 16; ++i)
             asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
     }
 
-    // ---- columnwise copy: packed column maxima over 16 rows, then over the lane pair
-    uint32_t cm[4] = {0u, 0u, 0u, 0u};
+    // ---- columnwise copy: the 32-row maximum joins the lane pair 8 lanes apart
+    //      (DPP row_ror:8 within each 16-lane row)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        cm[0] = absmax2(cm[0], v[i].x);
-        cm[1] = absmax2(cm[1], v[i].y);
-        cm[2] = absmax2(cm[2], v[i].z);
-        cm[3] = absmax2(cm[3], v[i].w);
-    }
+    for (int d = 0; d < 4; ++d)
+        cm[d] = pk_absmax(cm[d], (uint32_t)__builtin_amdgcn_mov_dpp((int)cm[d], 0x128, 0xF, 0xF, false));
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        const uint32_t other = (uint32_t)__shfl_xor((int)cm[d], 8, 64);
-        u16x2 a = __builtin_bit_cast(u16x2, cm[d]);
-        u16x2 b = __builtin_bit_cast(u16x2, other);
-        cm[d] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
-    }
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const uint32_t code0 = e8m0_code_from_bf16_mag(cm[d] & 0xFFFFu);   // column 2d
-        const uint32_t code1 = e8m0_code_from_bf16_mag(cm[d] >> 16);       // column 2d+1
-        const float sc0 = e8m0_decode(code0);
-        const float sc1 = e8m0_decode(code1);
+        const uint32_t code0 = mx_code(cm[d] & 0xFFFFu);   // column 2d
+        const uint32_t code1 = mx_code_hi(cm[d]);           // column 2d+1
+        const float sc0 = mx_scale(code0);
+        const float sc1 = mx_scale(code1);
         // Column-major pairs (row i, row i+1) of one column, built with one byte permute
         // each, so one scaled convert (one scale = the column's) encodes two rows.
         uint32_t a[4], b[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint32_t r0w = dword_of(v[4 * t + 0], d), r1w = dword_of(v[4 * t + 1], d);
-            const uint32_t r2w = dword_of(v[4 * t + 2], d), r3w = dword_of(v[4 * t + 3], d);
-            a[t] = cvt_e4m3x4_bf16(__builtin_amdgcn_perm(r1w, r0w, 0x05040100u),
-                                   __builtin_amdgcn_perm(r3w, r2w, 0x05040100u), sc0);
-            b[t] = cvt_e4m3x4_bf16(__builtin_amdgcn_perm(r1w, r0w, 0x07060302u),
-                                   __builtin_amdgcn_perm(r3w, r2w, 0x07060302u), sc1);
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t r0w = dword_of(v[4 * u + 0], d), r1w = dword_of(v[4 * u + 1], d);
+            const uint32_t r2w = dword_of(v[4 * u + 2], d), r3w = dword_of(v[4 * u + 3], d);
+            const uint32_t pa0 = __builtin_amdgcn_perm(r1w, r0w, 0x05040100u);
+            const uint32_t pa1 = __builtin_amdgcn_perm(r3w, r2w, 0x05040100u);
+            const uint32_t pb0 = __builtin_amdgcn_perm(r1w, r0w, 0x07060302u);
+            const uint32_t pb1 = __builtin_amdgcn_perm(r3w, r2w, 0x07060302u);
+            a[u] = cvt_e4m3x4_into(pa0, pa0, pa1, sc0);
+            b[u] = cvt_e4m3x4_into(pb0, pb0, pb1, sc1);
         }
         if (ok) {
-            const int64_t ka = col0 + 2 * d;
-            st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(q_col + ka * M + row0), make_uint4(a[0], a[1], a[2], a[3]));
-            st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(q_col + (ka + 1) * M + row0), make_uint4(b[0], b[1], b[2], b[3]));
+            st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(qc + (2 * d) * M + t.co),
+                                       make_uint4(a[0], a[1], a[2], a[3]));
+            st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(qc + (2 * d + 1) * M + t.co),
+                                       make_uint4(b[0], b[1], b[2], b[3]));
         }
-        if ((g & 1) == 0) {
-            lds_scol[lcol + 2 * d][lrow >> 5] = (uint8_t)code0;
-            lds_scol[lcol + 2 * d + 1][lrow >> 5] = (uint8_t)code1;
-        }
+        lds_scol[t.lcol + 2 * d][t.lrow >> 5] = (uint8_t)code0;      // the lane pair writes
+        lds_scol[t.lcol + 2 * d + 1][t.lrow >> 5] = (uint8_t)code1;  // one value each
     }
 
     __syncthreads();
-    // rowwise scales: one store of SROW_B bytes per row of the workgroup tile
+    // rowwise codes, staged in LDS: one 16-byte store per lane, so a store instruction
+    // writes whole rows of the workgroup tile (COLS bytes each) instead of each wave
+    // writing 64-byte halves of the lines of its own columns
+    if (ROW) {
+        constexpr int CHUNKS = G::COLS / 16;                  // 16-byte chunks per row
+        uint8_t* qr = q_row + rw * K + kw;
+#pragma unroll
+        for (int j = 0; j < G::ROWS * CHUNKS / G::THREADS; ++j) {
+            const int idx = j * G::THREADS + (int)threadIdx.x;
+            const int r = idx / CHUNKS, c16 = idx % CHUNKS;
+            const uint4 val = *reinterpret_cast<const uint4*>(&lds_q[r][16 * c16]);
+            if (FULL || (rw + r < M && kw + 16 * c16 < K))
+                st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(qr + (int64_t)r * K + 16 * c16), val);
+        }
+    }
+    // rowwise scales: SROW_B bytes per row of the workgroup tile
     if (ROW) {
         const int64_t nb_row = K >> 5;
         const int64_t b0 = kw >> 5;
-        const int nb = (int)min((int64_t)SROW_B, nb_row - b0);
-        for (int t = threadIdx.x; t < WG_ROWS; t += 64 * WR * WC) {
-            if (rw + t < M)
-                store_bytes<SROW_B>(s_row + (rw + t) * nb_row + b0, lds_srow[t], nb,
-                                    (nb_row % SROW_B) == 0);
+        const int nb = FULL ? G::SROW_B : (int)min((int64_t)G::SROW_B, nb_row - b0);
+        const bool al = FULL || ((nb == G::SROW_B) && (nb_row % G::SROW_B) == 0);
+#pragma unroll
+        for (int r = threadIdx.x; r < G::ROWS; r += G::THREADS) {
+            if (FULL || rw + r < M) {
+                uint8_t* dst = s_row + (rw + r) * nb_row + b0;
+                if (al) store_scales<G::SROW_B>(dst, lds_srow[r]);
+                else for (int j = 0; j < nb; ++j) dst[j] = lds_srow[r][j];
+            }
         }
     }
-    // columnwise scales: one store of SCOL_B bytes per column of the workgroup tile
+    // columnwise scales: SCOL_B bytes per column of the workgroup tile
     {
         const int64_t nb_col = M >> 5;
         const int64_t b0 = rw >> 5;
-        const int nb = (int)min((int64_t)SCOL_B, nb_col - b0);
-        for (int t = threadIdx.x; t < WG_COLS; t += 64 * WR * WC) {
-            if (kw + t < K)
-                store_bytes<SCOL_B>(s_col + (kw + t) * nb_col + b0, lds_scol[t], nb,
-                                    (nb_col % SCOL_B) == 0);
+        const int nb = FULL ? G::SCOL_B : (int)min((int64_t)G::SCOL_B, nb_col - b0);
+        const bool al = FULL || ((nb == G::SCOL_B) && (nb_col % G::SCOL_B) == 0);
+#pragma unroll
+        for (int c = threadIdx.x; c < G::COLS; c += G::THREADS) {
+            if (FULL || kw + c < K) {
+                uint8_t* dst = s_col + (kw + c) * nb_col + b0;
+                if (al) store_scales<G::SCOL_B>(dst, lds_scol[c]);
+                else for (int j = 0; j < nb; ++j) dst[j] = lds_scol[c][j];
+            }
         }
     }
-    __syncthreads();                           // LDS is reused by the next tile
 }
 
 // One workgroup tile per workgroup.
-template <bool ROW, int WR, int WC, int ORDER>
-__global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(4)))
+template <class G, bool ROW, bool FULL, typename OffT, int ORDER>
+__global__ __launch_bounds__(G::THREADS)
 void mx_quant_tile_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                           uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
                           uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
-                          int64_t col_groups, int64_t n_wg) {
-    __shared__ __align__(16) uint8_t lds_srow[TILE_ROWS * WR][TILE_COLS * WC / 32];
-    __shared__ __align__(16) uint8_t lds_scol[TILE_COLS * WC][TILE_ROWS * WR / 32];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+                          int64_t row_stripes, int64_t col_groups) {
+    __shared__ __align__(16) uint8_t lds_srow[G::ROWS][G::SROW_B];
+    __shared__ __align__(16) uint8_t lds_scol[G::COLS][G::SCOL_B];
+    __shared__ __align__(16) uint8_t lds_q[ROW ? G::ROWS : 1][G::QPITCH];
     int64_t rw, kw;
-    tile_origin<ORDER>(blockIdx.x, n_wg, col_groups, TILE_ROWS * WR, TILE_COLS * WC, rw, kw);
-    const int64_t row0 = rw + (wave / WC) * TILE_ROWS + 16 * (lane >> 3);
-    const int64_t col0 = kw + (wave % WC) * TILE_COLS + 8 * (lane & 7);
+    tile_origin<G, ORDER>(blockIdx.x, row_stripes, col_groups, rw, kw);
+    const TileLane<OffT> t = tile_lane<G, OffT>(M, K);
     uint4 v[16];
-    load_tile(v, x, K, row0, col0, row0 < M && col0 < K);
-    process_tile<ROW, WR, WC>(v, M, K, rw, kw, q_row, s_row, q_col, s_col, lds_srow, lds_scol);
+    load_tile<FULL>(v, x, M, K, rw, kw, t);
+    process_tile<G, ROW, FULL>(v, M, K, rw, kw, t, q_row, s_row, q_col, s_col, lds_srow, lds_scol, lds_q);
 }
 
 // Persistent variant: each workgroup walks tiles blockIdx.x, blockIdx.x + gridDim.x, ...
 // and issues the loads of its next tile before encoding the current one, so HBM reads
 // stay in flight while the codes are computed and stored.
-template <bool ROW, int WR, int WC, int ORDER>
-__global__ __launch_bounds__(64 * WR * WC) __attribute__((amdgpu_waves_per_eu(3)))
+template <class G, bool ROW, bool FULL, typename OffT, int ORDER>
+__global__ __launch_bounds__(G::THREADS)
 void mx_quant_tile_persistent_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                      uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
                                      uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
-                                     int64_t col_groups, int64_t n_wg) {
-    __shared__ __align__(16) uint8_t lds_srow[TILE_ROWS * WR][TILE_COLS * WC / 32];
-    __shared__ __align__(16) uint8_t lds_scol[TILE_COLS * WC][TILE_ROWS * WR / 32];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t lr = (wave / WC) * TILE_ROWS + 16 * (lane >> 3);
-    const int64_t lc = (wave % WC) * TILE_COLS + 8 * (lane & 7);
+                                     int64_t row_stripes, int64_t col_groups) {
+    __shared__ __align__(16) uint8_t lds_srow[G::ROWS][G::SROW_B];
+    __shared__ __align__(16) uint8_t lds_scol[G::COLS][G::SCOL_B];
+    __shared__ __align__(16) uint8_t lds_q[ROW ? G::ROWS : 1][G::QPITCH];
+    const int64_t n_wg = row_stripes * col_groups;
+    const TileLane<OffT> t = tile_lane<G, OffT>(M, K);
     int64_t w = blockIdx.x;
     if (w >= n_wg) return;                     // uniform over the workgroup
     int64_t rw, kw;
-    tile_origin<ORDER>(w, n_wg, col_groups, TILE_ROWS * WR, TILE_COLS * WC, rw, kw);
+    tile_origin<G, ORDER>(w, row_stripes, col_groups, rw, kw);
     uint4 v[16];
-    load_tile(v, x, K, rw + lr, kw + lc, rw + lr < M && kw + lc < K);
+    load_tile<FULL>(v, x, M, K, rw, kw, t);
     for (;;) {
         const int64_t wn = w + gridDim.x;
         int64_t rn = 0, kn = 0;
         uint4 vn[16];
         if (wn < n_wg) {
-            tile_origin<ORDER>(wn, n_wg, col_groups, TILE_ROWS * WR, TILE_COLS * WC, rn, kn);
-            load_tile(vn, x, K, rn + lr, kn + lc, rn + lr < M && kn + lc < K);
+            tile_origin<G, ORDER>(wn, row_stripes, col_groups, rn, kn);
+            load_tile<FULL>(vn, x, M, K, rn, kn, t);
         }
-        process_tile<ROW, WR, WC>(v, M, K, rw, kw, q_row, s_row, q_col, s_col, lds_srow, lds_scol);
+        process_tile<G, ROW, FULL>(v, M, K, rw, kw, t, q_row, s_row, q_col, s_col, lds_srow, lds_scol, lds_q);
         if (wn >= n_wg) break;
+        __syncthreads();                       // LDS is reused by the next tile
         w = wn;
         rw = rn;
         kw = kn;
@@ -330,32 +424,65 @@ void mx_quant_tile_persistent_kernel(const uint16_t* __restrict__ x, int64_t M, 
     }
 }
 
-template <bool ROW, int WR, int WC, int ORDER = 0>
-static void launch_tile(const void* x, int64_t M, int64_t K, void* q_row, void* s_row,
-                        void* q_col, void* s_col, hipStream_t stream, int64_t persistent_wgs = 0) {
-    const int64_t row_stripes = (M + TILE_ROWS * WR - 1) / (TILE_ROWS * WR);
-    const int64_t col_groups = (K + TILE_COLS * WC - 1) / (TILE_COLS * WC);
+template <class G, bool ROW, bool FULL, typename OffT, int ORDER>
+static void launch_tile_geom(const void* x, int64_t M, int64_t K, void* q_row, void* s_row, void* q_col,
+                             void* s_col, hipStream_t stream, int64_t persistent_wgs) {
+    const int64_t row_stripes = (M + G::ROWS - 1) / G::ROWS;
+    const int64_t col_groups = (K + G::COLS - 1) / G::COLS;
     const int64_t n_wg = row_stripes * col_groups;
     if (persistent_wgs > 0 && persistent_wgs < n_wg) {
-        hipLaunchKernelGGL((mx_quant_tile_persistent_kernel<ROW, WR, WC, ORDER>), dim3((unsigned)persistent_wgs),
-                           dim3(64 * WR * WC), 0, stream, (const uint16_t*)x, M, K, (uint8_t*)q_row,
-                           (uint8_t*)s_row, (uint8_t*)q_col, (uint8_t*)s_col, col_groups, n_wg);
+        hipLaunchKernelGGL((mx_quant_tile_persistent_kernel<G, ROW, FULL, OffT, ORDER>), dim3((unsigned)persistent_wgs),
+                           dim3(G::THREADS), 0, stream, (const uint16_t*)x, M, K, (uint8_t*)q_row,
+                           (uint8_t*)s_row, (uint8_t*)q_col, (uint8_t*)s_col, row_stripes, col_groups);
     } else {
-        hipLaunchKernelGGL((mx_quant_tile_kernel<ROW, WR, WC, ORDER>), dim3((unsigned)n_wg), dim3(64 * WR * WC),
+        hipLaunchKernelGGL((mx_quant_tile_kernel<G, ROW, FULL, OffT, ORDER>), dim3((unsigned)n_wg), dim3(G::THREADS),
                            0, stream, (const uint16_t*)x, M, K, (uint8_t*)q_row, (uint8_t*)s_row,
-                           (uint8_t*)q_col, (uint8_t*)s_col, col_groups, n_wg);
+                           (uint8_t*)q_col, (uint8_t*)s_col, row_stripes, col_groups);
     }
 }
 
-// Workgroup arrangement used by the library (wave tiles down x across), and the number of
-// persistent workgroups (one per compute unit of an MI355X) used once a tensor has more
-// tiles than that many workgroups can hold twice over.  Measured on the 65536 x 2048
-// activations: 130 us with one tile per workgroup, 114 us persistent with 256 workgroups
-// walking the tiles in row-stripe order (the tiles in flight then form one contiguous
-// band, so concurrent reads and the concurrent q_col writes of each k-row are contiguous).
-constexpr int TILE_WR = 1;
-constexpr int TILE_WC = 4;
-constexpr int TILE_PERSISTENT_WGS = 256;
+// Offsets inside one workgroup tile: x up to 2*ROWS*K bytes, q_col up to COLS*M bytes.
+template <class G>
+static bool tile_offsets_fit_32(int64_t M, int64_t K) {
+    return 2 * (int64_t)G::ROWS * K < (int64_t(1) << 31) && (int64_t)G::COLS * M < (int64_t(1) << 31);
+}
+
+template <class G, bool ROW, int ORDER>
+static void launch_tile(const void* x, int64_t M, int64_t K, void* q_row, void* s_row, void* q_col,
+                        void* s_col, hipStream_t stream, int64_t persistent_wgs) {
+    const bool full = (M % G::ROWS) == 0 && (K % G::COLS) == 0;
+    if (tile_offsets_fit_32<G>(M, K)) {
+        if (full) launch_tile_geom<G, ROW, true, uint32_t, ORDER>(x, M, K, q_row, s_row, q_col, s_col, stream, persistent_wgs);
+        else launch_tile_geom<G, ROW, false, uint32_t, ORDER>(x, M, K, q_row, s_row, q_col, s_col, stream, persistent_wgs);
+    } else {
+        if (full) launch_tile_geom<G, ROW, true, int64_t, ORDER>(x, M, K, q_row, s_row, q_col, s_col, stream, persistent_wgs);
+        else launch_tile_geom<G, ROW, false, int64_t, ORDER>(x, M, K, q_row, s_row, q_col, s_col, stream, persistent_wgs);
+    }
+}
+
+// Geometry, tile order and persistent workgroup count used by the library (0 = one tile
+// per workgroup always; otherwise used once a tensor has more than twice as many tiles).
+// Measured on the 65536 x 2048 activations (dual, one launch after a 512 MiB read):
+// 1x4 row-band 105.6 us with 256 persistent workgroups, 106.2 us with one tile per
+// workgroup; 2x2 106.5, 1x8 108.2, 2x4 115.5; column-band order 138-170.  With the same
+// loads and stores and no arithmetic at all the pattern takes 102-113 us, and a plain
+// copy of the same byte count 93 us with these non-temporal stores, so the kernel runs
+// at the speed of its access pattern.
+#ifndef BSQ_TILE_WR
+#define BSQ_TILE_WR 1
+#endif
+#ifndef BSQ_TILE_WC
+#define BSQ_TILE_WC 4
+#endif
+#ifndef BSQ_TILE_ORDER
+#define BSQ_TILE_ORDER 0
+#endif
+#ifndef BSQ_TILE_PERSISTENT_WGS
+#define BSQ_TILE_PERSISTENT_WGS 256
+#endif
+using LibTile = TileGeom<BSQ_TILE_WR, BSQ_TILE_WC>;
+constexpr int TILE_ORDER = BSQ_TILE_ORDER;
+constexpr int TILE_PERSISTENT_WGS = BSQ_TILE_PERSISTENT_WGS;
 
 // ----------------------------------------------------------------------------- dequant
 
@@ -428,13 +555,12 @@ hipError_t launch_mx_quant(const void* x, int64_t M, int64_t K, int mode,
                            stream, (const uint4*)x, (uint2*)q_row, (uint8_t*)s_row, n_chunks);
         return hipGetLastError();
     }
-    const int64_t n_wg = ((M + TILE_ROWS * TILE_WR - 1) / (TILE_ROWS * TILE_WR)) *
-                         ((K + TILE_COLS * TILE_WC - 1) / (TILE_COLS * TILE_WC));
+    const int64_t n_wg = ((M + LibTile::ROWS - 1) / LibTile::ROWS) * ((K + LibTile::COLS - 1) / LibTile::COLS);
     const int64_t pw = (n_wg > 2 * TILE_PERSISTENT_WGS) ? TILE_PERSISTENT_WGS : 0;
     if (mode == 3)
-        launch_tile<true, TILE_WR, TILE_WC, 1>(x, M, K, q_row, s_row, q_col, s_col, stream, pw);
+        launch_tile<LibTile, true, TILE_ORDER>(x, M, K, q_row, s_row, q_col, s_col, stream, pw);
     else
-        launch_tile<false, TILE_WR, TILE_WC, 1>(x, M, K, nullptr, nullptr, q_col, s_col, stream, pw);
+        launch_tile<LibTile, false, TILE_ORDER>(x, M, K, nullptr, nullptr, q_col, s_col, stream, pw);
     return hipGetLastError();
 }
 
