@@ -85,45 +85,85 @@ void nv_check_offsets_kernel(const int64_t* __restrict__ off, int64_t E, int64_t
     check_offsets(off, E, R, status);
 }
 
-// One wave per row, the row held in registers: NS slots of 64 lanes x 8 BF16 (so rows of
-// up to 512*NS elements).  Lane l of slot j holds elements 512 j + 8 l .. +7; a 1x16
-// block is the lane pair (2i, 2i+1).
+// One wave per span of RPW consecutive rows (RPW = 1 or 2), the span held in registers:
+// NS slots of 64 lanes x 8 BF16 (so spans of up to 512*NS elements).  Lane l of slot j
+// holds chunk 64 j + l of the span (elements 8 (64 j + l) .. +7); a 1x16 block is the
+// lane pair (2i, 2i+1), and since K % 16 == 0 no block straddles two rows.  Two short
+// rows per wave keep every lane busy and twice the bytes in flight per wave (K = 768:
+// 192 chunks fill 3 slots exactly, where one row would leave half of its second slot
+// idle).
 constexpr int NV_WAVES = 4;
 
-// Wave index as a scalar: all address arithmetic of a row is then wave-uniform and the
+// Wave index as a scalar: all address arithmetic of a span is then wave-uniform and the
 // per-lane part is a 32-bit offset.
 __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
-// FULL: the row is exactly NS slots long (K == 512 NS), so no lane is ever out of range.
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+
+// Max over the whole wave of both 16-bit halves independently (two rows' maxima at once),
+// returned uniform; same DPP pattern as wave_max.
+__device__ __forceinline__ uint32_t wave_max_pk(uint32_t v) {
+    v = pk_max_u16(v, dpp_xor1(v));
+    v = pk_max_u16(v, dpp_xor2(v));
+    v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true));  // row_half_mirror
+    v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true));  // row_mirror
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return pk_max_u16(pk_max_u16(a, b), pk_max_u16(c, d));
+}
+
+// FULL: the span is exactly NS slots long (RPW * K == 512 NS and all RPW rows exist), so
+// no lane is ever out of range.
 template <int NS, bool FULL>
-__device__ __forceinline__ void load_row(uint4 (&v)[NS], const uint4* __restrict__ xr, int cpr) {
+__device__ __forceinline__ void load_span(uint4 (&v)[NS], const uint4* __restrict__ xs, int n_ch) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
         const int ch = 64 * j + lane;
-        v[j] = (FULL || ch < cpr) ? ld_stream<NVQ_NT_LOAD>(xr + ch) : make_uint4(0u, 0u, 0u, 0u);
+        v[j] = (FULL || ch < n_ch) ? ld_stream<NVQ_NT_LOAD>(xs + ch) : make_uint4(0u, 0u, 0u, 0u);
     }
 }
 
-// Quantize one row held in v (all lanes of the wave take part).  The row's block-scale
-// bytes are gathered in the wave's LDS slice `lsb` (32 NS bytes) and leave as 16-byte
-// stores when the row's scale run is 16-byte aligned.
-template <int NS, bool FULL>
-__device__ __forceinline__ void quant_row(const uint4 (&v)[NS], int64_t row, int64_t K, int cpr,
-                                          uint32_t* __restrict__ q, uint8_t* __restrict__ sb,
-                                          float* __restrict__ st, uint8_t* lsb) {
+// Quantize the span held in v (all lanes of the wave take part): rows r0 .. r0+RPW-1,
+// n_ch valid chunks.  The span's block-scale bytes are gathered in the wave's LDS slice
+// `lsb` (32 NS bytes) and leave as 16-byte stores when the run is 16-byte aligned.
+template <int NS, int RPW, bool FULL>
+__device__ __forceinline__ void quant_span(const uint4 (&v)[NS], int64_t r0, int n_ch, int cpr,
+                                           uint32_t* __restrict__ q, uint8_t* __restrict__ sb,
+                                           float* __restrict__ st, uint8_t* lsb) {
+    static_assert(RPW == 1 || RPW == 2, "one or two rows per wave");
     const int lane = threadIdx.x & 63;
-    uint32_t m = 0u;
-#pragma unroll
-    for (int j = 0; j < NS; ++j) m = max(m, chunk_absmax8(v[j]));
-    const uint32_t amax_t = wave_max(m);
-    const float s_t = __uint_as_float(amax_t << 16) / 2688.0f;     // fl(amax / (6 * 448))
-    const float p = 6.0f * s_t;                                     // fl(6 s_t)
+    // second row of the span for slot j? (RPW == 2 only; cpr is the row length in chunks)
+    auto in_b = [&](int j) { return RPW == 2 && 64 * j + lane >= cpr; };
 
-    uint32_t* qr = q + row * cpr;                     // 4 bytes of q per chunk
-    uint8_t* sbr = sb + row * (K >> 4);
+    float s_a, s_b = 0.0f;
+    if (RPW == 1) {
+        uint32_t m = 0u;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) m = max(m, chunk_absmax8(v[j]));
+        s_a = __uint_as_float(wave_max(m) << 16) / 2688.0f;          // fl(amax / (6 * 448))
+    } else {
+        uint32_t m = 0u;                                              // row a low, row b high
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const uint32_t c = chunk_absmax8(v[j]);
+            m = pk_max_u16(m, in_b(j) ? (c << 16) : c);
+        }
+        const uint32_t mm = wave_max_pk(m);
+        s_a = __uint_as_float(mm << 16) / 2688.0f;
+        s_b = __uint_as_float(mm & 0xFFFF0000u) / 2688.0f;
+    }
+    const float p_a = 6.0f * s_a, p_b = 6.0f * s_b;                   // fl(6 s_t)
+
+    uint32_t* qs = q + r0 * cpr;                      // 4 bytes of q per chunk
+    uint8_t* sbs = sb + r0 * (cpr >> 1);              // one scale byte per chunk pair
     const bool odd = (lane & 1) != 0;
     // Slots are taken two at a time: the two lanes of a block pair hold both blocks'
     // maxima, the even lane works out slot j's scale and multiplier, the odd lane slot
@@ -134,8 +174,10 @@ __device__ __forceinline__ void quant_row(const uint4 (&v)[NS], int64_t row, int
         const bool two = j + 1 < NS;
         const uint32_t a0 = pair_max(chunk_absmax8(v[j]));
         const uint32_t a1 = two ? pair_max(chunk_absmax8(v[j + 1])) : 0u;
+        const int jj = (two && odd) ? j + 1 : j;                      // slot this lane works out
+        const bool b = in_b(jj);
         float f;
-        const uint32_t code = nv_block_scale((two && odd) ? a1 : a0, s_t, p, f);
+        const uint32_t code = nv_block_scale((two && odd) ? a1 : a0, b ? s_b : s_a, b ? p_b : p_a, f);
         uint32_t code0 = code, code1 = code;
         float f0 = f, f1 = f;
         if (two) {
@@ -148,34 +190,32 @@ __device__ __forceinline__ void quant_row(const uint4 (&v)[NS], int64_t row, int
         }
         const int ch0 = 64 * j + lane;
         const uint32_t packed0 = nv_enc8(v[j], f0);
-        if (FULL || ch0 < cpr) st_stream<NVQ_NT_STORE>(qr + ch0, packed0);
+        if (FULL || ch0 < n_ch) st_stream<NVQ_NT_STORE>(qs + ch0, packed0);
         if (!odd) lsb[32 * j + (lane >> 1)] = (uint8_t)code0;
         if (two) {
             const int ch1 = 64 * (j + 1) + lane;
             const uint32_t packed1 = nv_enc8(v[j + 1], f1);
-            if (FULL || ch1 < cpr) st_stream<NVQ_NT_STORE>(qr + ch1, packed1);
+            if (FULL || ch1 < n_ch) st_stream<NVQ_NT_STORE>(qs + ch1, packed1);
             if (!odd) lsb[32 * (j + 1) + (lane >> 1)] = (uint8_t)code1;
         }
     }
-    if (lane == 0) st[row] = s_t;
+    if (lane == 0) st[r0] = s_a;
+    if (RPW == 2 && lane == 1 && n_ch > cpr) st[r0 + 1] = s_b;
     // the wave's LDS slice: written above by even lanes, read below by the first lanes
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int nsb = cpr >> 1;                         // scale bytes of the row
-    if ((nsb & 15) == 0) {
+    const int nsb = n_ch >> 1;                        // scale bytes of the span
+    if ((nsb & 15) == 0 && ((r0 * (cpr >> 1)) & 15) == 0) {
         if (lane < (nsb >> 4))
-            st_stream<NVQ_NT_STORE>(reinterpret_cast<uint4*>(sbr) + lane, reinterpret_cast<const uint4*>(lsb)[lane]);
+            st_stream<NVQ_NT_STORE>(reinterpret_cast<uint4*>(sbs) + lane, reinterpret_cast<const uint4*>(lsb)[lane]);
     } else {
-        for (int i = lane; i < nsb; i += 64) sbr[i] = lsb[i];
+        for (int i = lane; i < nsb; i += 64) sbs[i] = lsb[i];
     }
-    // the slice is rewritten by the wave's next row
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
 }
 
-// One row per wave.
-template <int NS, bool FULL>
+// One span per wave.
+template <int NS, int RPW, bool FULL>
 __global__ __launch_bounds__(64 * NV_WAVES)
 void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
                           uint8_t* __restrict__ sb, float* __restrict__ st,
@@ -184,44 +224,14 @@ void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
                           int32_t* __restrict__ status) {
     const int wave = wave_id();
     if (status != nullptr && blockIdx.x == 0 && wave == 0) check_offsets(offsets, E, R, status);
-    const int64_t row = (int64_t)blockIdx.x * NV_WAVES + wave;
-    if (row >= R) return;
+    const int64_t r0 = ((int64_t)blockIdx.x * NV_WAVES + wave) * RPW;
+    if (r0 >= R) return;
     __shared__ __align__(16) uint8_t lds_sb[NV_WAVES][32 * NS];
     const int cpr = (int)(K >> 3);                    // 8-element chunks per row
+    const int n_ch = (RPW == 2 && r0 + 1 >= R) ? cpr : RPW * cpr;
     uint4 v[NS];
-    load_row<NS, FULL>(v, x + row * cpr, cpr);
-    quant_row<NS, FULL>(v, row, K, cpr, q, sb, st, lds_sb[wave]);
-}
-
-// Persistent waves: wave w takes rows w, w + W, w + 2W, ... (W waves in the grid) and
-// loads its next row before quantizing the current one, so reads stay in flight while
-// the codes are computed and stored.
-template <int NS, bool FULL>
-__global__ __launch_bounds__(64 * NV_WAVES)
-void nv_quant_rows_persistent_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
-                                     uint8_t* __restrict__ sb, float* __restrict__ st,
-                                     int64_t R, int64_t K,
-                                     const int64_t* __restrict__ offsets, int64_t E,
-                                     int32_t* __restrict__ status) {
-    const int wave = wave_id();
-    if (status != nullptr && blockIdx.x == 0 && wave == 0) check_offsets(offsets, E, R, status);
-    const int64_t stride = (int64_t)gridDim.x * NV_WAVES;
-    int64_t row = (int64_t)blockIdx.x * NV_WAVES + wave;
-    if (row >= R) return;
-    __shared__ __align__(16) uint8_t lds_sb[NV_WAVES][32 * NS];
-    const int cpr = (int)(K >> 3);
-    uint4 v[NS];
-    load_row<NS, FULL>(v, x + row * cpr, cpr);
-    for (;;) {
-        const int64_t next = row + stride;
-        uint4 vn[NS];
-        if (next < R) load_row<NS, FULL>(vn, x + next * cpr, cpr);
-        quant_row<NS, FULL>(v, row, K, cpr, q, sb, st, lds_sb[wave]);
-        if (next >= R) break;
-        row = next;
-#pragma unroll
-        for (int j = 0; j < NS; ++j) v[j] = vn[j];
-    }
+    load_span<NS, FULL>(v, x + r0 * cpr, n_ch);
+    quant_span<NS, RPW, FULL>(v, r0, n_ch, cpr, q, sb, st, lds_sb[wave]);
 }
 
 // Rows longer than the register-resident variants: two passes over the row (the second
@@ -331,34 +341,27 @@ void nv_dequant_kernel(const uint32_t* __restrict__ q, const uint8_t* __restrict
 
 // ----------------------------------------------------------------------------- launch
 
-// Persistent workgroups for long row lists (0 = one row per wave).
-constexpr int64_t NV_PERSISTENT_WGS = 0;
-
-template <int NS, bool FULL>
-static void launch_rows_full(const void* x, int64_t R, int64_t K, void* q, void* sb, float* st,
-                             const int64_t* off, int64_t E, int32_t* status, hipStream_t stream,
-                             int64_t persistent_wgs) {
-    const int64_t grid = (R + NV_WAVES - 1) / NV_WAVES;
-    if (persistent_wgs > 0 && grid > 2 * persistent_wgs) {
-        hipLaunchKernelGGL((nv_quant_rows_persistent_kernel<NS, FULL>), dim3((unsigned)persistent_wgs),
-                           dim3(64 * NV_WAVES), 0, stream, (const uint4*)x, (uint32_t*)q,
-                           (uint8_t*)sb, st, R, K, off, E, status);
-    } else {
-        hipLaunchKernelGGL((nv_quant_rows_kernel<NS, FULL>), dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
-                           stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, st, R, K, off, E,
-                           status);
-    }
-}
-
-template <int NS>
+// Spans of RPW rows per wave; FULL when every span fills its NS slots exactly (the last
+// span of an odd row count under RPW = 2 takes the bounds-checked kernel).
+template <int NS, int RPW>
 static void launch_rows(const void* x, int64_t R, int64_t K, void* q, void* sb, float* st,
-                        const int64_t* off, int64_t E, int32_t* status, hipStream_t stream,
-                        int64_t persistent_wgs = NV_PERSISTENT_WGS) {
-    if (K == 512 * NS)
-        launch_rows_full<NS, true>(x, R, K, q, sb, st, off, E, status, stream, persistent_wgs);
+                        const int64_t* off, int64_t E, int32_t* status, hipStream_t stream) {
+    const int64_t spans = (R + RPW - 1) / RPW;
+    const int64_t grid = (spans + NV_WAVES - 1) / NV_WAVES;
+    const bool full = RPW * K == 512 * NS && R % RPW == 0;
+    if (full)
+        hipLaunchKernelGGL((nv_quant_rows_kernel<NS, RPW, true>), dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
+                           stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, st, R, K, off, E, status);
     else
-        launch_rows_full<NS, false>(x, R, K, q, sb, st, off, E, status, stream, persistent_wgs);
+        hipLaunchKernelGGL((nv_quant_rows_kernel<NS, RPW, false>), dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
+                           stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, st, R, K, off, E, status);
 }
+
+// Rows of at most this many elements go two to a wave.
+#ifndef BSQ_NV_PAIR_MAX_K
+#define BSQ_NV_PAIR_MAX_K 768
+#endif
+constexpr int64_t NV_PAIR_MAX_K = BSQ_NV_PAIR_MAX_K;
 
 hipError_t launch_nv_quant(const void* x, int64_t R, int64_t K, void* q, void* sb, float* st,
                            const int64_t* offsets, int64_t E, int32_t* status,
@@ -372,13 +375,22 @@ hipError_t launch_nv_quant(const void* x, int64_t R, int64_t K, void* q, void* s
                                status);
         return hipGetLastError();
     }
+    if (K <= NV_PAIR_MAX_K) {
+        switch ((2 * (K / 8) + 63) / 64) {
+            case 1: launch_rows<1, 2>(x, R, K, q, sb, st, offsets, E, status, stream); break;
+            case 2: launch_rows<2, 2>(x, R, K, q, sb, st, offsets, E, status, stream); break;
+            case 3: launch_rows<3, 2>(x, R, K, q, sb, st, offsets, E, status, stream); break;
+            default: launch_rows<4, 2>(x, R, K, q, sb, st, offsets, E, status, stream); break;
+        }
+        return hipGetLastError();
+    }
     switch (slots) {
-        case 1: launch_rows<1>(x, R, K, q, sb, st, offsets, E, status, stream); break;
-        case 2: launch_rows<2>(x, R, K, q, sb, st, offsets, E, status, stream); break;
-        case 3: launch_rows<3>(x, R, K, q, sb, st, offsets, E, status, stream); break;
-        case 4: launch_rows<4>(x, R, K, q, sb, st, offsets, E, status, stream); break;
-        case 5: case 6: launch_rows<6>(x, R, K, q, sb, st, offsets, E, status, stream); break;
-        case 7: case 8: launch_rows<8>(x, R, K, q, sb, st, offsets, E, status, stream); break;
+        case 1: launch_rows<1, 1>(x, R, K, q, sb, st, offsets, E, status, stream); break;
+        case 2: launch_rows<2, 1>(x, R, K, q, sb, st, offsets, E, status, stream); break;
+        case 3: launch_rows<3, 1>(x, R, K, q, sb, st, offsets, E, status, stream); break;
+        case 4: launch_rows<4, 1>(x, R, K, q, sb, st, offsets, E, status, stream); break;
+        case 5: case 6: launch_rows<6, 1>(x, R, K, q, sb, st, offsets, E, status, stream); break;
+        case 7: case 8: launch_rows<8, 1>(x, R, K, q, sb, st, offsets, E, status, stream); break;
         default:
             hipLaunchKernelGGL(nv_quant_rows_long_kernel, dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
                                stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, st, R, K,

@@ -61,6 +61,26 @@ def test_mx_colwise_and_both_match_oracle(M, K, mode):
         assert np.all(qr.payload() == 0xA5) and np.all(sr.payload() == 0xA5)
 
 
+def test_mx_both_on_a_tensor_with_tiles_beyond_31_bit_offsets():
+    """M = 2^23 + 32 rows: a workgroup tile of the columnwise copy then spans more than
+    2^31 bytes of q_col, so the kernel addresses with 64-bit offsets (and the tile grid
+    is ragged in both directions)."""
+    M, K = (1 << 23) + 32, 32
+    log("mx both %dx%d" % (M, K))
+    rng = np.random.default_rng(23)
+    x = rng.integers(0, 1 << 16, size=(M, K), dtype=np.uint16)
+    x[(x & 0x7F80) == 0x7F80] &= 0xBFFF                       # finite inputs only
+    x[rng.integers(0, M, size=4096)] = 0                       # some all-zero rows
+    qr, sr, qc, sc = _mx_gpu(x, bsq.MX_BOTH)
+    eqc, esc = oracle.mx_quantize_colwise(x)
+    assert_same("q_col", qc.payload().reshape(K, M), eqc)
+    assert_same("s_col", sc.payload().reshape(K, M // 32), esc)
+    del eqc, esc
+    eqr, esr = oracle.mx_quantize_rowwise(x)
+    assert_same("q_row", qr.payload().reshape(M, K), eqr)
+    assert_same("s_row", sr.payload().reshape(M, K // 32), esr)
+
+
 def test_mx_rowwise_differs_from_colwise_on_gpu():
     """The handmade 32x32 example: row 0 all 1024, the rest 0.01 (see tests/golden)."""
     x = np.full((32, 32), 0x3C24, np.uint16)
@@ -94,8 +114,10 @@ def test_mx_dequant_round_trip_matches_oracle(M, K):
     assert_same("mx dequant", bits(y), oracle.mx_dequantize(eq, es))
 
 
-NV_SHAPES = [(1, 16), (5, 32), (3, 48), (9, 512), (17, 768), (4, 1040), (33, 2048),
-             (2, 4096), (3, 4112), (2, 8208)]
+# short rows go two to a wave: odd row counts leave a one-row tail span, and even counts
+# with K = 256, 512, 768 fill whole register slots
+NV_SHAPES = [(1, 16), (5, 32), (3, 48), (8, 64), (6, 256), (9, 512), (10, 512), (17, 768),
+             (16, 768), (2, 768), (4, 1040), (33, 2048), (2, 4096), (3, 4112), (2, 8208)]
 
 
 @pytest.mark.parametrize("R,K", NV_SHAPES)
