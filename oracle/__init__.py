@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         for name in ("oracle_mx_quantize_rowwise", "oracle_mx_quantize_colwise"):
             getattr(L, name).restype = None
             getattr(L, name).argtypes = [P, I64, I64, P, P]
+        L.oracle_mx_quantize_colwise_grouped.restype = None
+        L.oracle_mx_quantize_colwise_grouped.argtypes = [P, I64, I64, P, I64, P, P, I64]
         L.oracle_mx_dequantize.restype = None
         L.oracle_mx_dequantize.argtypes = [P, P, I64, I64, P]
         L.oracle_nv_quantize_per_token.restype = None
@@ -206,6 +208,35 @@ def mx_quantize_colwise(x: np.ndarray):
     s = np.empty((K, M // 32), np.uint8)
     lib().oracle_mx_quantize_colwise(_ptr(x), M, K, _ptr(q), _ptr(s))
     return q, s
+
+
+def mx_group_blocks(offsets) -> np.ndarray:
+    """Per-expert block counts ceil(m_e / 32) of a grouped columnwise copy."""
+    m = np.diff(np.asarray(offsets, dtype=np.int64))
+    return (m + 31) // 32
+
+
+def mx_quantize_colwise_grouped(x: np.ndarray, offsets, s_ld=None):
+    """Grouped columnwise MXFP8 of x[M][K] over expert segments offsets int64[E+1]: 32x1
+    blocks confined to each segment, a partial last block per segment.  Returns
+    (q_col[K][M], s_col[K][s_ld], ok); s_ld defaults to the total block count.  ok is
+    False (and the arrays None) when the offsets are invalid or s_ld is too small."""
+    x = _as_bf16_bits(x)
+    M, K = x.shape
+    off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    ok = bool(off.ndim == 1 and off.size >= 2 and off[0] == 0 and off[-1] == M
+              and np.all(np.diff(off) >= 0))
+    if not ok:
+        return None, None, False
+    nb = int(mx_group_blocks(off).sum())
+    s_ld = nb if s_ld is None else int(s_ld)
+    if s_ld < nb:
+        return None, None, False
+    q = np.empty((K, M), np.uint8)
+    s = np.empty((K, s_ld), np.uint8)
+    lib().oracle_mx_quantize_colwise_grouped(_ptr(x), M, K, _ptr(off), off.size - 1,
+                                             _ptr(q), _ptr(s), s_ld)
+    return q, s, True
 
 
 def mx_dequantize(q: np.ndarray, s: np.ndarray) -> np.ndarray:

@@ -196,16 +196,22 @@ uint8_t oracle_e8m0_code(double amax) {
     return (uint8_t)(e + 127);
 }
 
-/* One 32-element block: values v[0..31] (exact BF16 values), codes to q[i*qs]. */
-static uint8_t mx_block(const double* v, uint8_t* q, int64_t qs) {
+/* One block of n <= 32 elements (32 except for the partial last block of an expert
+ * segment, see the grouped columnwise copy below): values v[0..n-1] (exact BF16
+ * values), codes to q[i*qs].  The scale depends only on the largest magnitude. */
+static uint8_t mx_block_n(const double* v, int n, uint8_t* q, int64_t qs) {
     double amax = 0.0;
-    for (int i = 0; i < 32; ++i)
+    for (int i = 0; i < n; ++i)
         if (fabs(v[i]) > amax) amax = fabs(v[i]);
     uint8_t c = oracle_e8m0_code(amax);
     double inv_scale = ldexp(1.0, 127 - (int)c);       /* 2^-e, exact */
-    for (int i = 0; i < 32; ++i)
+    for (int i = 0; i < n; ++i)
         q[i * qs] = oracle_enc_e4m3(v[i] * inv_scale);  /* exact product */
     return c;
+}
+
+static uint8_t mx_block(const double* v, uint8_t* q, int64_t qs) {
+    return mx_block_n(v, 32, q, qs);
 }
 
 /* Rowwise MXFP8 of x[rows][cols] (BF16 bits): blocks of 32 along cols.
@@ -238,6 +244,39 @@ void oracle_mx_quantize_colwise(const uint16_t* x, int64_t M, int64_t K,
             for (int i = 0; i < 32; ++i)
                 v[i] = oracle_bf16_to_double(x[(b * 32 + i) * K + k]);
             s_col[k * nb + b] = mx_block(v, q_col + k * M + b * 32, 1);
+        }
+    }
+}
+
+/* Grouped columnwise MXFP8 for the weight-gradient operand of MoE experts (MXFP8
+ * recipe: experts are MXFP8 and the weight-gradient GEMM runs in MXFP8 on the
+ * columnwise copy; section "Recipe 1: end-to-end MXFP8 RL").  The rows of x[M][K]
+ * are E consecutive expert segments [off[e], off[e+1]); an expert's GEMM reduces
+ * over its own rows only, so a 32x1 block never crosses a segment.  Expert e's rows
+ * form nb_e = ceil(m_e / 32) blocks of 32 consecutive rows from off[e]; the last one
+ * holds the remaining m_e mod 32 rows when m_e is not a multiple of 32, and its scale
+ * is taken over the rows present.  Layout: q_col[K][M] as in the flat copy (expert
+ * e's copy is entries off[e] .. off[e+1]-1 of every row); s_col[K][s_ld], expert e's
+ * blocks at entries blk_e .. blk_e + nb_e - 1 of every row, blk_e = nb_0 + ... +
+ * nb_(e-1).  With every m_e a multiple of 32 this is exactly the flat copy.  The
+ * offsets must be valid (off[0] = 0, non-decreasing, off[E] = M) and s_ld at least
+ * the total block count; the caller checks both. */
+void oracle_mx_quantize_colwise_grouped(const uint16_t* x, int64_t M, int64_t K,
+                                        const int64_t* off, int64_t E,
+                                        uint8_t* q_col, uint8_t* s_col, int64_t s_ld) {
+    build_tables();
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k) {
+        double v[32];
+        int64_t blk = 0;
+        for (int64_t e = 0; e < E; ++e) {
+            for (int64_t r0 = off[e]; r0 < off[e + 1]; r0 += 32) {
+                const int n = (off[e + 1] - r0 < 32) ? (int)(off[e + 1] - r0) : 32;
+                for (int i = 0; i < n; ++i)
+                    v[i] = oracle_bf16_to_double(x[(r0 + i) * K + k]);
+                s_col[k * s_ld + blk] = mx_block_n(v, n, q_col + k * M + r0, 1);
+                ++blk;
+            }
         }
     }
 }

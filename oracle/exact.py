@@ -220,6 +220,36 @@ def mx_quantize_colwise(x: Sequence[Sequence[int]]):
     return mx_quantize_rowwise(xt)
 
 
+def mx_block_partial(bits: Sequence[int]) -> Tuple[int, List[int]]:
+    """A block of 1 to 32 BF16 patterns (the last block of an expert segment may hold
+    fewer than 32 rows) -> (E8M0 code, its E4M3 codes); the scale is set by the largest
+    magnitude present."""
+    assert 1 <= len(bits) <= 32
+    vals = [bf16_value(b) for b in bits]
+    amax = max(v for _, v in vals)
+    c = e8m0_code(amax)
+    scale = _pow2(c - 127)
+    return c, [enc_e4m3(s, v / scale) for s, v in vals]
+
+
+def mx_quantize_colwise_grouped(x: Sequence[Sequence[int]], offsets: Sequence[int]):
+    """Grouped columnwise copy: for each expert, the columnwise blocks of that expert's
+    rows alone, 32 rows at a time from the segment start (the last block partial).
+    Returns (q_col as K lists of M codes, K lists of scale codes in expert order)."""
+    M, K = len(x), len(x[0])
+    q = [[None] * M for _ in range(K)]
+    s = [[] for _ in range(K)]
+    for e in range(len(offsets) - 1):
+        lo, hi = offsets[e], offsets[e + 1]
+        for k in range(K):
+            column = [x[r][k] for r in range(lo, hi)]
+            for b in range(0, hi - lo, 32):
+                c, codes = mx_block_partial(column[b:b + 32])
+                s[k].append(c)
+                q[k][lo + b:lo + b + len(codes)] = codes
+    return q, s
+
+
 def mx_dequant_one(q: int, c: int) -> int:
     v = e4m3_value(q)
     sc = e8m0_value(c)

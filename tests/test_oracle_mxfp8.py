@@ -228,3 +228,89 @@ def test_config1_zero_block_and_outliers():
     assert s[r, b] == 0 and np.all((q[r, 32 * b:32 * b + 32] & 0x7F) == 0)
     # the x1000 outliers lift their blocks' scales about log2(1000) ~ 10 codes
     assert int(s.max()) - int(np.median(s)) >= 7
+
+
+# --------------------------------------------------------------------------- grouped colwise
+
+def _rand_bf16(rng, rows, cols):
+    x = rng.integers(0, 1 << 16, size=(rows, cols), dtype=np.uint16)
+    x[(x & 0x7F80) == 0x7F80] &= 0xBFFF                   # finite only
+    return x
+
+
+def _parse_ranges(items):
+    out = {}
+    for it in items:
+        where, val = it.split(":")
+        lo, _, hi = where.partition("-")
+        for r in range(int(lo), int(hi or lo) + 1):
+            out[r] = int(val, 16)
+    return out
+
+
+def test_grouped_colwise_golden():
+    g = _read_golden("mx_grouped_colwise.txt")
+    M = int(g["rows"][0])
+    off = [int(v) for v in g["offsets"]]
+    xr, codes = _parse_ranges(g["x_rows"]), _parse_ranges(g["codes"])
+    x = np.array([[xr[r]] * 32 for r in range(M)], np.uint16)
+    q, s, ok = oracle.mx_quantize_colwise_grouped(x, off)
+    assert ok and s.shape == (32, 3)
+    assert np.all(s == np.array([int(v, 16) for v in g["scales"]], np.uint8))
+    assert np.all(q == np.array([codes[r] for r in range(M)], np.uint8))
+
+
+def test_grouped_colwise_with_aligned_segments_is_the_flat_copy():
+    rng = np.random.default_rng(11)
+    x = _rand_bf16(rng, 256, 64)
+    for off in ([0, 256], [0, 32, 32, 96, 256], [0, 0, 128, 128, 224, 256]):
+        q, s, ok = oracle.mx_quantize_colwise_grouped(x, off)
+        qf, sf = oracle.mx_quantize_colwise(x)
+        assert ok
+        assert np.array_equal(q, qf) and np.array_equal(s, sf)
+
+
+def test_grouped_colwise_partial_block_equals_zero_padded_segment():
+    """Zero rows never raise a block maximum, so an expert's partial last block has the
+    scale and codes of the flat columnwise copy of its segment padded with zero rows."""
+    rng = np.random.default_rng(12)
+    off = [0, 5, 5, 45, 77, 109, 110]
+    x = _rand_bf16(rng, off[-1], 32)
+    q, s, ok = oracle.mx_quantize_colwise_grouped(x, off)
+    assert ok
+    blk = 0
+    for e in range(len(off) - 1):
+        lo, hi = off[e], off[e + 1]
+        m = hi - lo
+        if m == 0:
+            continue
+        pad = np.zeros(((m + 31) // 32 * 32, 32), np.uint16)
+        pad[:m] = x[lo:hi]
+        qf, sf = oracle.mx_quantize_colwise(pad)
+        nb = sf.shape[1]
+        assert np.array_equal(q[:, lo:hi], qf[:, :m]), e
+        assert np.array_equal(s[:, blk:blk + nb], sf), e
+        blk += nb
+    assert blk == s.shape[1]
+
+
+def test_grouped_colwise_matches_exact_checker():
+    rng = np.random.default_rng(13)
+    off = [0, 3, 3, 40, 41, 75]
+    x = _rand_bf16(rng, off[-1], 4)
+    x[1] = 0                                              # an all-zero row inside a block
+    q, s, ok = oracle.mx_quantize_colwise_grouped(x, off)
+    eq, es = exact.mx_quantize_colwise_grouped(x.tolist(), off)
+    assert ok
+    assert q.tolist() == eq
+    assert s.tolist() == es
+
+
+def test_grouped_colwise_rejects_bad_offsets_and_short_scale_rows():
+    x = np.zeros((64, 32), np.uint16)
+    for off in ([1, 64], [0, 40, 30, 64], [0, 63], [0, 65]):
+        assert oracle.mx_quantize_colwise_grouped(x, off)[2] is False
+    # offsets [0, 1, 64]: ceil(1/32) + ceil(63/32) = 3 blocks per column
+    assert oracle.mx_quantize_colwise_grouped(x, [0, 1, 64], s_ld=2)[2] is False
+    q, s, ok = oracle.mx_quantize_colwise_grouped(x, [0, 1, 64], s_ld=3)
+    assert ok and s.shape == (32, 3) and np.all(s == 0) and np.all(q == 0)
