@@ -320,8 +320,24 @@ def all_configs(torch, bsq, workloads, dev, reps=21):
     a, w = bf(c5["a"]), bf(c5["w"])
     run(5, "activations", a, "mx_both")
     run(5, "weights", w, "mx_both")
-    run(5, "routed rows", a.index_select(0, torch.from_numpy(c5["token_idx"]).to(dev)), "nv",
-        torch.from_numpy(c5["offsets"]).to(dev))
+    x = a.index_select(0, torch.from_numpy(c5["token_idx"]).to(dev))
+    off = torch.from_numpy(c5["offsets"]).to(dev)
+    run(5, "routed rows", x, "nv", off)
+    # the same routed rows as the MoE weight-gradient operand: MXFP8 with 32x1 blocks
+    # confined to each expert's rows (partial last blocks), rowwise copy fused or not
+    M, K = x.shape
+    nb = int(((np.diff(c5["offsets"]) + 31) // 32).sum())
+    s_ld = bsq.mx_group_scale_entries(M, off.numel() - 1)
+    u8 = torch.uint8
+    g_out = (torch.empty(M, K, dtype=u8, device=dev), torch.empty(M, K // 32, dtype=u8, device=dev),
+             torch.empty(K, M, dtype=u8, device=dev), torch.empty(K, s_ld, dtype=u8, device=dev),
+             torch.zeros(1, dtype=torch.int32, device=dev))
+    col_bytes = 2 * M * K + M * K + K * nb
+    report(5, "mxfp8 grouped dual quant routed rows", "%dx%d" % (M, K), col_bytes + M * K + M * K // 32, M * K,
+           lambda: bsq.mx_quantize_mxfp8_grouped(x, off, "both", s_ld, *g_out, stream=stream))
+    report(5, "mxfp8 grouped columnwise quant routed rows", "%dx%d" % (M, K), col_bytes, M * K,
+           lambda: bsq.mx_quantize_mxfp8_grouped(x, off, "colwise", s_ld, None, None, *g_out[2:], stream=stream))
+    torch.cuda.synchronize()
 
 
 def cpu_baseline(a_np, w_np, tok, frac):

@@ -10,6 +10,7 @@ error.
 Layouts (all row-major, all on the GPU):
   MXFP8 rowwise     q_row u8 [M, K]      s_row u8 [M, K/32]   (E4M3 / E8M0)
   MXFP8 columnwise  q_col u8 [K, M]      s_col u8 [K, M/32]   (stored transposed)
+  MXFP8 grouped     q_col u8 [K, M]      s_col u8 [K, s_ld]   (32x1 blocks per expert)
   NVFP4 per token   q u8 [R, K/2]        sb u8 [R, K/16]      st f32 [R]
 BF16 tensors are ``torch.bfloat16``.
 """
@@ -66,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.nv_quantize_nvfp4_per_token.argtypes = [P, I64, I64, P, P, P, P]
         L.nv_quantize_nvfp4_per_token_grouped.restype = I32
         L.nv_quantize_nvfp4_per_token_grouped.argtypes = [P, I64, I64, P, I64, P, P, P, P, P]
+        L.mx_quantize_mxfp8_grouped.restype = I32
+        L.mx_quantize_mxfp8_grouped.argtypes = [P, I64, I64, I32, P, I64, P, P, P, P, I64, P, P]
         L.mx_dequantize.restype = I32
         L.mx_dequantize.argtypes = [P, P, I64, I64, P, P]
         L.nv_dequantize.restype = I32
@@ -147,6 +150,46 @@ def mx_quantize_mxfp8(x: torch.Tensor, mode="both", q_row=None, s_row=None, q_co
            lib().mx_quantize_mxfp8(_ptr(x), M, K, m, _ptr(q_row), _ptr(s_row), _ptr(q_col),
                                    _ptr(s_col), _stream(stream)))
     return q_row, s_row, q_col, s_col
+
+
+def mx_group_scale_entries(M: int, E: int) -> int:
+    """Scale entries per column that any expert offsets of M rows and E experts fit in."""
+    return (M + 31 * E) // 32
+
+
+def mx_quantize_mxfp8_grouped(x: torch.Tensor, expert_offsets: torch.Tensor, mode="colwise",
+                              s_ld=None, q_row=None, s_row=None, q_col=None, s_col=None,
+                              status=None, stream=None):
+    """MXFP8 of x [M, K] bf16 with 32x1 blocks confined to expert segments (expert_offsets
+    int64 [E+1] on the GPU).  mode "colwise" | "both".  s_ld defaults to a length that any
+    offsets fit in.  Returns (q_row, s_row, q_col, s_col, status); status is a device
+    int32 [1] the kernel sets to BSQ_OK or BSQ_ERR_OFFSETS (read it after synchronising)."""
+    m = _MODES.get(mode)
+    if m not in (MX_COLWISE, MX_BOTH):
+        raise ValueError("mode must be 'colwise' or 'both', got %r" % (mode,))
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    M, K = x.shape
+    _dev_tensor(x, "x", torch.bfloat16, (M, K))
+    if expert_offsets.dim() != 1 or expert_offsets.numel() < 2:
+        raise ValueError("expert_offsets must be int64 [E+1] with E >= 1")
+    E = expert_offsets.numel() - 1
+    _dev_tensor(expert_offsets, "expert_offsets", torch.int64, (E + 1,))
+    if K % 32:
+        raise ValueError("MXFP8 needs K % 32 == 0")
+    if s_ld is None:
+        s_ld = mx_group_scale_entries(M, E)
+    row = m == MX_BOTH
+    q_row = _out(q_row, "q_row", torch.uint8, (M, K), x) if row else None
+    s_row = _out(s_row, "s_row", torch.uint8, (M, K // 32), x) if row else None
+    q_col = _out(q_col, "q_col", torch.uint8, (K, M), x)
+    s_col = _out(s_col, "s_col", torch.uint8, (K, s_ld), x)
+    status = _out(status, "status", torch.int32, (1,), x)
+    _check("mx_quantize_mxfp8_grouped",
+           lib().mx_quantize_mxfp8_grouped(_ptr(x), M, K, m, _ptr(expert_offsets), E,
+                                           _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col),
+                                           s_ld, _ptr(status), _stream(stream)))
+    return q_row, s_row, q_col, s_col, status
 
 
 def nv_quantize_nvfp4_per_token(x: torch.Tensor, q=None, sb=None, st=None, stream=None):

@@ -12,6 +12,9 @@
 namespace bsq {
 hipError_t launch_mx_quant(const void* x, int64_t M, int64_t K, int mode, void* q_row,
                            void* s_row, void* q_col, void* s_col, hipStream_t stream);
+hipError_t launch_mx_quant_grouped(const void* x, int64_t M, int64_t K, int mode, const int64_t* off,
+                                   int64_t E, void* q_row, void* s_row, void* q_col, void* s_col,
+                                   int64_t s_ld, int32_t* status, hipStream_t stream);
 hipError_t launch_mx_dequant(const void* q, const void* s, int64_t rows, int64_t cols, void* y,
                              hipStream_t stream);
 hipError_t launch_nv_quant(const void* x, int64_t R, int64_t K, void* q, void* sb, float* st,
@@ -92,6 +95,41 @@ int mx_quantize_mxfp8(const void* x, int64_t M, int64_t K, int mode, void* q_row
     if (overlap(bufs, 5)) return BSQ_ERR_ALIAS;
     return hip_status(bsq::launch_mx_quant(x, M, K, mode, q_row, s_row, q_col, s_col,
                                            static_cast<hipStream_t>(stream)));
+}
+
+int mx_quantize_mxfp8_grouped(const void* x, int64_t M, int64_t K, int mode,
+                              const int64_t* expert_offsets, int64_t E, void* q_row, void* s_row,
+                              void* q_col, void* s_col, int64_t s_ld, int32_t* status_dev,
+                              void* stream) {
+    if (mode != MX_COLWISE && mode != MX_BOTH) return BSQ_ERR_MODE;
+    const bool row = mode == MX_BOTH;
+    if (!size_ok(M, K, 2)) return BSQ_ERR_SHAPE;
+    if (K % 32 != 0) return BSQ_ERR_SHAPE;
+    if (E < 1 || E >= (int64_t(1) << 31)) return BSQ_ERR_SHAPE;
+    const int64_t min_blocks = (M + 31) / 32;
+    if (min_blocks + E >= (int64_t(1) << 31)) return BSQ_ERR_SHAPE;
+    if (s_ld < min_blocks || !size_ok(K, s_ld, 1)) return BSQ_ERR_SHAPE;
+    if (expert_offsets == nullptr) return BSQ_ERR_NULL;
+    if (misaligned(expert_offsets, 8)) return BSQ_ERR_ALIGN;
+    if (status_dev != nullptr && misaligned(status_dev, 4)) return BSQ_ERR_ALIGN;
+    const bool empty = (M == 0 || K == 0);
+    if (empty && status_dev == nullptr) return BSQ_OK;
+    if (!empty) {
+        if (x == nullptr || q_col == nullptr || s_col == nullptr) return BSQ_ERR_NULL;
+        if (row && (q_row == nullptr || s_row == nullptr)) return BSQ_ERR_NULL;
+        if (misaligned(x, 16) || misaligned(q_col, 16) || misaligned(s_col, 16)) return BSQ_ERR_ALIGN;
+        if (row && (misaligned(q_row, 16) || misaligned(s_row, 16))) return BSQ_ERR_ALIGN;
+    }
+    const int64_t n = empty ? 0 : M * K;
+    const Buf bufs[7] = {{x, 2 * n},
+                         {q_row, row ? n : 0}, {s_row, row ? n / 32 : 0},
+                         {q_col, n}, {s_col, empty ? 0 : K * s_ld},
+                         {expert_offsets, 8 * (E + 1)},
+                         {status_dev, status_dev != nullptr ? 4 : 0}};
+    if (overlap(bufs, 7)) return BSQ_ERR_ALIAS;
+    return hip_status(bsq::launch_mx_quant_grouped(x, M, K, mode, expert_offsets, E, q_row, s_row,
+                                                   q_col, s_col, s_ld, status_dev,
+                                                   static_cast<hipStream_t>(stream)));
 }
 
 static int nv_quant_common(const void* x, int64_t R, int64_t K, const int64_t* offsets, int64_t E,

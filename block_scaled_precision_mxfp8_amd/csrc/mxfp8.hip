@@ -195,6 +195,66 @@ __device__ __forceinline__ uint32_t cvt_e4m3x4_into(uint32_t spare, uint32_t w0,
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// One 16-byte chunk (8 BF16 of one row) of a tile: folds its magnitudes into the lane's
+// packed column maxima cm (two columns per dword) and, for the rowwise copy, returns its
+// 8 E4M3 codes and the E8M0 code of its 1x32 block (the quad of lanes of the row).
+template <bool ROW>
+__device__ __forceinline__ uint2 tile_row_chunk(const uint4& v, uint32_t (&cm)[4], uint32_t& code) {
+    const uint32_t a0 = v.x & 0x7FFF7FFFu, a1 = v.y & 0x7FFF7FFFu;
+    const uint32_t a2 = v.z & 0x7FFF7FFFu, a3 = v.w & 0x7FFF7FFFu;
+    cm[0] = pk_absmax(cm[0], a0);
+    cm[1] = pk_absmax(cm[1], a1);
+    cm[2] = pk_absmax(cm[2], a2);
+    cm[3] = pk_absmax(cm[3], a3);
+    if (!ROW) return make_uint2(0u, 0u);
+    const uint32_t m = pk_absmax(pk_absmax(a0, a1), pk_absmax(a2, a3));
+    code = mx_code_hi(quad_max(pk_fold(m)));
+    const float sc = mx_scale(code);
+    return make_uint2(cvt_e4m3x4_into(a0, v.x, v.y, sc), cvt_e4m3x4_into(a2, v.z, v.w, sc));
+}
+
+// The lane's packed column maxima over its 16 rows joined with the partner lane 8 apart
+// (the other 16 rows of the 32-row block; DPP row_ror:8 within each 16-lane row).
+__device__ __forceinline__ void tile_join_pairs(uint32_t (&cm)[4]) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+        cm[d] = pk_absmax(cm[d], (uint32_t)__builtin_amdgcn_mov_dpp((int)cm[d], 0x128, 0xF, 0xF, false));
+}
+
+// Columnwise codes of dword d of the lane's 16 rows: columns 2d (a, code0) and 2d+1 (b,
+// code1), 16 rows each in row order.  Column-major pairs (row i, row i+1) of one column
+// are built with one byte permute each, so one scaled convert (one scale = the column's)
+// encodes two rows.
+__device__ __forceinline__ void tile_col_codes(const uint4 (&v)[16], uint32_t cmd, int d, uint4& a, uint4& b,
+                                               uint32_t& code0, uint32_t& code1) {
+    code0 = mx_code(cmd & 0xFFFFu);
+    code1 = mx_code_hi(cmd);
+    const float sc0 = mx_scale(code0);
+    const float sc1 = mx_scale(code1);
+    uint32_t ra[4], rb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint32_t r0w = dword_of(v[4 * u + 0], d), r1w = dword_of(v[4 * u + 1], d);
+        const uint32_t r2w = dword_of(v[4 * u + 2], d), r3w = dword_of(v[4 * u + 3], d);
+        const uint32_t pa0 = __builtin_amdgcn_perm(r1w, r0w, 0x05040100u);
+        const uint32_t pa1 = __builtin_amdgcn_perm(r3w, r2w, 0x05040100u);
+        const uint32_t pb0 = __builtin_amdgcn_perm(r1w, r0w, 0x07060302u);
+        const uint32_t pb1 = __builtin_amdgcn_perm(r3w, r2w, 0x07060302u);
+        ra[u] = cvt_e4m3x4_into(pa0, pa0, pa1, sc0);
+        rb[u] = cvt_e4m3x4_into(pb0, pb0, pb1, sc1);
+    }
+    a = make_uint4(ra[0], ra[1], ra[2], ra[3]);
+    b = make_uint4(rb[0], rb[1], rb[2], rb[3]);
+}
+
+// The compiler would otherwise keep row-pass temporaries of the packed tile alive into
+// the column pass (doubling the live tile); this empty register barrier pins the tile.
+__device__ __forceinline__ void tile_pin(uint4 (&v)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
+}
+
 // Workgroup tile w -> first row and first column.
 //   ORDER 0: row stripes in order, column groups fastest (the tiles in flight form one
 //            band of full rows: contiguous reads and q_row writes)
@@ -260,60 +320,25 @@ __device__ __forceinline__ void process_tile(uint4 (&v)[16], int64_t M, int64_t 
     uint32_t cm[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const uint32_t a0 = v[i].x & 0x7FFF7FFFu, a1 = v[i].y & 0x7FFF7FFFu;
-        const uint32_t a2 = v[i].z & 0x7FFF7FFFu, a3 = v[i].w & 0x7FFF7FFFu;
-        cm[0] = pk_absmax(cm[0], a0);
-        cm[1] = pk_absmax(cm[1], a1);
-        cm[2] = pk_absmax(cm[2], a2);
-        cm[3] = pk_absmax(cm[3], a3);
+        uint32_t code = 0u;
+        const uint2 out = tile_row_chunk<ROW>(v[i], cm, code);
         if (ROW) {
-            const uint32_t m = pk_absmax(pk_absmax(a0, a1), pk_absmax(a2, a3));
-            const uint32_t code = mx_code_hi(quad_max(pk_fold(m)));
-            const float sc = mx_scale(code);
-            const uint2 out = make_uint2(cvt_e4m3x4_into(a0, v[i].x, v[i].y, sc),
-                                         cvt_e4m3x4_into(a2, v[i].z, v[i].w, sc));
             *reinterpret_cast<uint2*>(&lds_q[t.lrow + i][t.lcol]) = out;
             lds_srow[t.lrow + i][t.lcol >> 5] = (uint8_t)code;   // the quad writes one value
         }
     }
-    if (ROW) {
-        // The column pass below re-reads the packed tile; this empty register barrier keeps
-        // the compiler from carrying row-pass temporaries into it instead.
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
-    }
+    if (ROW) tile_pin(v);
 
-    // ---- columnwise copy: the 32-row maximum joins the lane pair 8 lanes apart
-    //      (DPP row_ror:8 within each 16-lane row)
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-        cm[d] = pk_absmax(cm[d], (uint32_t)__builtin_amdgcn_mov_dpp((int)cm[d], 0x128, 0xF, 0xF, false));
+    // ---- columnwise copy
+    tile_join_pairs(cm);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        const uint32_t code0 = mx_code(cm[d] & 0xFFFFu);   // column 2d
-        const uint32_t code1 = mx_code_hi(cm[d]);           // column 2d+1
-        const float sc0 = mx_scale(code0);
-        const float sc1 = mx_scale(code1);
-        // Column-major pairs (row i, row i+1) of one column, built with one byte permute
-        // each, so one scaled convert (one scale = the column's) encodes two rows.
-        uint32_t a[4], b[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t r0w = dword_of(v[4 * u + 0], d), r1w = dword_of(v[4 * u + 1], d);
-            const uint32_t r2w = dword_of(v[4 * u + 2], d), r3w = dword_of(v[4 * u + 3], d);
-            const uint32_t pa0 = __builtin_amdgcn_perm(r1w, r0w, 0x05040100u);
-            const uint32_t pa1 = __builtin_amdgcn_perm(r3w, r2w, 0x05040100u);
-            const uint32_t pb0 = __builtin_amdgcn_perm(r1w, r0w, 0x07060302u);
-            const uint32_t pb1 = __builtin_amdgcn_perm(r3w, r2w, 0x07060302u);
-            a[u] = cvt_e4m3x4_into(pa0, pa0, pa1, sc0);
-            b[u] = cvt_e4m3x4_into(pb0, pb0, pb1, sc1);
-        }
+        uint4 a, b;
+        uint32_t code0, code1;
+        tile_col_codes(v, cm[d], d, a, b, code0, code1);
         if (ok) {
-            st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(qc + (2 * d) * M + t.co),
-                                       make_uint4(a[0], a[1], a[2], a[3]));
-            st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(qc + (2 * d + 1) * M + t.co),
-                                       make_uint4(b[0], b[1], b[2], b[3]));
+            st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(qc + (2 * d) * M + t.co), a);
+            st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(qc + (2 * d + 1) * M + t.co), b);
         }
         lds_scol[t.lcol + 2 * d][t.lrow >> 5] = (uint8_t)code0;      // the lane pair writes
         lds_scol[t.lcol + 2 * d + 1][t.lrow >> 5] = (uint8_t)code1;  // one value each
@@ -483,6 +508,246 @@ static void launch_tile(const void* x, int64_t M, int64_t K, void* q_row, void* 
 using LibTile = TileGeom<BSQ_TILE_WR, BSQ_TILE_WC>;
 constexpr int TILE_ORDER = BSQ_TILE_ORDER;
 constexpr int TILE_PERSISTENT_WGS = BSQ_TILE_PERSISTENT_WGS;
+
+// ----------------------------------------------------------------------------- grouped col / both
+
+// Columnwise (and dual) MXFP8 over expert segments of the rows, for the weight-gradient
+// operand of MoE experts.  Page "Towards Blackwell-native 8-bit and 4-bit RL", section
+// "Recipe 1: end-to-end MXFP8 RL": the experts run in MXFP8 including the weight-gradient
+// GEMM, whose operand is the columnwise copy, and each expert's GEMM reduces over its own
+// rows only.  So a 32x1 block never crosses an expert boundary: expert e's m_e rows form
+// ceil(m_e / 32) blocks from its first row, the last one partial when m_e % 32 != 0 (its
+// scale comes from the rows present).  Blocks are numbered in row order over all experts;
+// q_col keeps the flat [K][M] layout and s_col[K][s_ld] holds block n at entry n of every
+// row.  The rowwise copy is row-local, identical to the flat one.
+//
+// A workgroup (4 waves side by side, 256 columns) takes 4 consecutive blocks, which cover
+// one contiguous range of at most 128 rows; one wave finds them with a scan of the
+// segment lengths.  The wave layout is the flat tile's: a lane pair owns one block (16
+// rows each); rows past the end of a partial block are loaded as copies of its last row,
+// which leaves the block maximum unchanged, and are not stored.  Columnwise codes go out
+// as one 16-byte store per lane and column (at any byte alignment: segments start at any
+// row) or byte stores for the part of a partial block.  Block indices are 32-bit
+// (ceil(M/32) + E < 2^31, checked by the caller).
+constexpr int GROUP_BLOCKS = 4;
+
+struct GroupTable {
+    int64_t start[GROUP_BLOCKS];   // first row of each of the workgroup's blocks
+    int32_t len[GROUP_BLOCKS];     // its row count (1..32), 0 past the last block
+};
+
+__device__ __forceinline__ int64_t clamp_row(int64_t r, int64_t M) { return r < 0 ? 0 : (r > M ? M : r); }
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+// Wave 0: locate blocks n0 .. n0+3 (block n exists if n < min(total, n_limit)).  Offsets
+// are clamped into [0, M] so that even invalid offsets never address outside the tensor.
+__device__ void group_find_blocks(const int64_t* __restrict__ off, int64_t E, int64_t M,
+                                  int64_t n0, int64_t n_limit, GroupTable& tab) {
+    const int lane = threadIdx.x & 63;
+    if (lane < GROUP_BLOCKS) { tab.start[lane] = 0; tab.len[lane] = 0; }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    int64_t base = 0;                                   // blocks of the experts before e0
+    for (int64_t e0 = 0; e0 < E && base < n0 + GROUP_BLOCKS; e0 += 64) {
+        const int64_t e = e0 + lane;
+        const int64_t lo = e < E ? clamp_row(off[e], M) : M;
+        const int64_t hi = e < E ? clamp_row(off[e + 1], M) : M;
+        const int32_t c = hi > lo ? (int32_t)((hi - lo + 31) >> 5) : 0;
+        const int32_t incl = wave_incl_scan(c);
+        const int64_t excl = base + (incl - c);
+#pragma unroll
+        for (int h = 0; h < GROUP_BLOCKS; ++h) {
+            const int64_t n = n0 + h;
+            if (c > 0 && n < n_limit && excl <= n && n < excl + c) {
+                const int64_t r = lo + 32 * (n - excl);
+                if (r < hi) {                            // always, unless the offsets are garbage
+                    tab.start[h] = r;
+                    tab.len[h] = (int32_t)(hi - r < 32 ? hi - r : 32);
+                }
+            }
+        }
+        base += __shfl(incl, 63, 64);
+    }
+}
+
+// Wave 0 of workgroup 0: offsets valid (o[0] = 0, non-decreasing, o[E] = M) and the
+// total block count within s_ld?
+__device__ void group_check(const int64_t* __restrict__ off, int64_t E, int64_t M, int64_t s_ld,
+                            int32_t* __restrict__ status) {
+    const int lane = threadIdx.x & 63;
+    bool bad = false;
+    int64_t blocks = 0;
+    for (int64_t e = lane; e < E; e += 64) {
+        const int64_t lo = off[e], hi = off[e + 1];
+        bad |= hi < lo;
+        if (hi > lo) blocks += (hi - lo + 31) >> 5;
+    }
+    if (lane == 0) bad |= (off[0] != 0) || (off[E] != M);
+    for (int o = 32; o > 0; o >>= 1) blocks += __shfl_xor(blocks, o, 64);
+    bad |= blocks > s_ld;
+    const bool any_bad = __any(bad);
+    if (lane == 0) *status = any_bad ? 6 /* BSQ_ERR_OFFSETS */ : 0;
+}
+
+template <bool ROW>
+__global__ __launch_bounds__(256)
+void mx_quant_grouped_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                             const int64_t* __restrict__ off, int64_t E,
+                             uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
+                             uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col, int64_t s_ld,
+                             int64_t n_limit, int64_t col_groups, int32_t* __restrict__ status) {
+    using G = TileGeom<1, 4>;
+    __shared__ GroupTable tab;
+    __shared__ __align__(16) uint8_t lds_srow[G::ROWS][G::SROW_B];
+    __shared__ __align__(16) uint8_t lds_scol[G::COLS][GROUP_BLOCKS];
+    __shared__ __align__(16) uint8_t lds_q[ROW ? G::ROWS : 1][G::QPITCH];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t quad = blockIdx.x / col_groups;
+    const int64_t kw = (blockIdx.x - quad * col_groups) * G::COLS;
+    if (wave == 0) group_find_blocks(off, E, M, GROUP_BLOCKS * quad, n_limit, tab);
+    if (wave == 1 && status != nullptr && blockIdx.x == 0) group_check(off, E, M, s_ld, status);
+    __syncthreads();
+    if (tab.len[0] == 0) return;                       // uniform: no block left for this quad
+    const int64_t row0 = tab.start[0];                 // the quad's rows: row0 .. row0 + L - 1
+    int L = 0;
+#pragma unroll
+    for (int h = 0; h < GROUP_BLOCKS; ++h) L += tab.len[h];
+
+    const int g = lane >> 3, c = lane & 7;
+    const int h = g >> 1, half = g & 1;
+    const int lcol = wave * TILE_COLS + 8 * c;
+    const int64_t col = kw + lcol;
+    const bool colok = col < K;
+    const int blen = tab.len[h];
+    const int64_t bstart = blen > 0 ? tab.start[h] : row0;
+    const int vc = min(max(blen - 16 * half, 0), 16);  // rows of this lane inside its block
+    const int last = (blen > 0 ? blen : 1) - 1;        // last row of the block (offset)
+    const int pos0 = (int)(bstart - row0) + 16 * half; // lane's first row inside the quad's range
+
+    uint4 v[16];
+    {
+        const uint16_t* xc = x + (colok ? col : kw);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int ri = min(16 * half + i, last);
+            v[i] = ld_stream<MXTILE_NT_LOAD>(reinterpret_cast<const uint4*>(xc + (bstart + ri) * K));
+        }
+    }
+
+    uint32_t cm[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        uint32_t code = 0u;
+        const uint2 out = tile_row_chunk<ROW>(v[i], cm, code);
+        // (with valid offsets the quad's blocks are contiguous and 0 <= pos0 + i < 128;
+        //  the bound only keeps invalid offsets inside the staging buffer)
+        if (ROW && i < vc && (unsigned)(pos0 + i) < (unsigned)G::ROWS) {
+            *reinterpret_cast<uint2*>(&lds_q[pos0 + i][lcol]) = out;
+            lds_srow[pos0 + i][lcol >> 5] = (uint8_t)code;
+        }
+    }
+    if (ROW) tile_pin(v);
+
+    tile_join_pairs(cm);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        uint4 a, b;
+        uint32_t code0, code1;
+        tile_col_codes(v, cm[d], d, a, b, code0, code1);
+        if (colok && vc > 0) {
+            uint8_t* pa = q_col + (col + 2 * d) * M + bstart + 16 * half;
+            uint8_t* pb = pa + M;
+            if (vc == 16) {
+                __builtin_memcpy(pa, &a, 16);          // any byte alignment
+                __builtin_memcpy(pb, &b, 16);
+            } else {
+                const uint8_t* ba = reinterpret_cast<const uint8_t*>(&a);
+                const uint8_t* bb = reinterpret_cast<const uint8_t*>(&b);
+                for (int j = 0; j < vc; ++j) { pa[j] = ba[j]; pb[j] = bb[j]; }
+            }
+        }
+        if (blen > 0) {
+            lds_scol[lcol + 2 * d][h] = (uint8_t)code0;     // the lane pair writes one value
+            lds_scol[lcol + 2 * d + 1][h] = (uint8_t)code1;
+        }
+    }
+    __syncthreads();
+
+    if (ROW) {
+        // rowwise codes of the quad's L rows, whole 256-byte row segments per store
+        constexpr int CHUNKS = G::COLS / 16;
+        for (int idx = threadIdx.x; idx < L * CHUNKS; idx += G::THREADS) {
+            const int r = idx / CHUNKS, c16 = idx % CHUNKS;
+            if (kw + 16 * c16 < K && row0 + r < M) {
+                const uint4 val = *reinterpret_cast<const uint4*>(&lds_q[r][16 * c16]);
+                st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(q_row + (row0 + r) * K + kw + 16 * c16), val);
+            }
+        }
+        const int64_t nb_row = K >> 5;
+        const int nb = (int)min((int64_t)G::SROW_B, nb_row - (kw >> 5));
+        for (int r = threadIdx.x; r < L && row0 + r < M; r += G::THREADS) {
+            uint8_t* dst = s_row + (row0 + r) * nb_row + (kw >> 5);
+            if (nb == G::SROW_B && (nb_row % G::SROW_B) == 0) store_scales<G::SROW_B>(dst, lds_srow[r]);
+            else for (int j = 0; j < nb; ++j) dst[j] = lds_srow[r][j];
+        }
+    }
+    // columnwise scales: blocks 4 quad .. of every column of the workgroup
+    {
+        int nblk = 0;
+#pragma unroll
+        for (int hh = 0; hh < GROUP_BLOCKS; ++hh) nblk += tab.len[hh] > 0 ? 1 : 0;
+        const int t = threadIdx.x;
+        if (kw + t < K) {
+            uint8_t* dst = s_col + (kw + t) * s_ld + GROUP_BLOCKS * quad;
+            if (nblk == GROUP_BLOCKS && (s_ld % GROUP_BLOCKS) == 0)
+                *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(lds_scol[t]);
+            else
+                for (int j = 0; j < nblk; ++j) dst[j] = lds_scol[t][j];
+        }
+    }
+}
+
+__global__ __launch_bounds__(64)
+void mx_group_check_kernel(const int64_t* __restrict__ off, int64_t E, int64_t M, int64_t s_ld,
+                           int32_t* __restrict__ status) {
+    group_check(off, E, M, s_ld, status);
+}
+
+hipError_t launch_mx_quant_grouped(const void* x, int64_t M, int64_t K, int mode, const int64_t* off,
+                                   int64_t E, void* q_row, void* s_row, void* q_col, void* s_col,
+                                   int64_t s_ld, int32_t* status, hipStream_t stream) {
+    // blocks that can exist: at most one per row, at most ceil(m_e/32) per expert, at most s_ld
+    int64_t n_limit = (M + 31 * E) / 32;
+    if (n_limit > M) n_limit = M;
+    if (n_limit > s_ld) n_limit = s_ld;
+    if (n_limit == 0 || K == 0) {
+        if (status != nullptr)
+            hipLaunchKernelGGL(mx_group_check_kernel, dim3(1), dim3(64), 0, stream, off, E, M, s_ld, status);
+        return hipGetLastError();
+    }
+    const int64_t col_groups = (K + 255) / 256;
+    const int64_t quads = (n_limit + GROUP_BLOCKS - 1) / GROUP_BLOCKS;
+    const int64_t grid = quads * col_groups;
+    if (mode == 3)
+        hipLaunchKernelGGL(mx_quant_grouped_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream,
+                           (const uint16_t*)x, M, K, off, E, (uint8_t*)q_row, (uint8_t*)s_row,
+                           (uint8_t*)q_col, (uint8_t*)s_col, s_ld, n_limit, col_groups, status);
+    else
+        hipLaunchKernelGGL(mx_quant_grouped_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream,
+                           (const uint16_t*)x, M, K, off, E, nullptr, nullptr,
+                           (uint8_t*)q_col, (uint8_t*)s_col, s_ld, n_limit, col_groups, status);
+    return hipGetLastError();
+}
 
 // ----------------------------------------------------------------------------- dequant
 

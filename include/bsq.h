@@ -111,6 +111,39 @@ int nv_quantize_nvfp4_per_token_grouped(const void* x_bf16, int64_t R, int64_t K
                                         int32_t* status_dev, void* stream);
 
 /*
+ * MXFP8 quantization of x[M][K] (BF16) whose rows are grouped by expert, for the MoE
+ * weight-gradient operand: rows [offsets[e], offsets[e+1]) belong to expert e.
+ * Passages: "Recipe 1: end-to-end MXFP8 RL" (MoE experts run in MXFP8, the weight-gradient
+ * GEMM included, on the columnwise copy quantized from full precision) and "Format
+ * background" (32-value blocks, E8M0 scale rounded up).  An expert's GEMM reduces over
+ * its own rows only, so a 32x1 block never crosses an expert boundary: expert e's
+ * m_e = offsets[e+1] - offsets[e] rows form ceil(m_e / 32) blocks of 32 consecutive rows
+ * starting at offsets[e]; when m_e % 32 != 0 the last one is partial and its scale is
+ * taken over the rows present.  Scale and code rules are those of mx_quantize_mxfp8.
+ * Blocks are numbered n = 0, 1, ... in row order over all experts.
+ *
+ * mode MX_COLWISE or MX_BOTH (MX_ROWWISE is plain mx_quantize_mxfp8: rowwise blocks never
+ * cross rows, so grouping does not change them).  Needs K % 32 == 0; M may be any size.
+ *   q_col u8 [K][M] E4M3, the flat columnwise layout (expert e's copy is entries
+ *         offsets[e] .. offsets[e+1]-1 of every row);
+ *   s_col u8 [K][s_ld] E8M0, block n at entry n of every row (expert e's blocks follow
+ *         those of experts 0 .. e-1); entries past the last block are not written;
+ *   q_row, s_row (MX_BOTH only): exactly as mx_quantize_mxfp8's rowwise copy.
+ * With every m_e a multiple of 32 and s_ld = M/32 the bytes equal mx_quantize_mxfp8's.
+ * s_ld >= ceil(M/32) (the fewest blocks any offsets give); (M + 31 E) / 32 is enough for
+ * any offsets; ceil(M/32) + E < 2^31.
+ * expert_offsets: DEVICE int64 [E+1], E >= 1, checked on the device without any host
+ * synchronisation: if status_dev is not NULL the kernel writes BSQ_ERR_OFFSETS to
+ * *status_dev when offsets[0] != 0, offsets[E] != M, the offsets decrease, or the blocks
+ * need more than s_ld scale entries, and BSQ_OK otherwise.  With invalid offsets the
+ * output bytes are unspecified, but nothing outside the given buffers is written.
+ */
+int mx_quantize_mxfp8_grouped(const void* x_bf16, int64_t M, int64_t K, int mode,
+                              const int64_t* expert_offsets, int64_t E,
+                              void* q_row, void* s_row, void* q_col, void* s_col, int64_t s_ld,
+                              int32_t* status_dev, void* stream);
+
+/*
  * MXFP8 dequantization to BF16, in the stored layout: q u8 [rows][cols] E4M3 and
  * s u8 [rows][cols/32] E8M0 (blocks of 32 along the stored last dimension).
  * Passage: "High-precision and dequantized backward" (backward GEMMs consume BF16

@@ -41,7 +41,7 @@ def _declared_functions():
 
 def test_header_declares_the_expected_entry_points():
     names = _declared_functions()
-    for n in ("mx_quantize_mxfp8", "nv_quantize_nvfp4_per_token",
+    for n in ("mx_quantize_mxfp8", "mx_quantize_mxfp8_grouped", "nv_quantize_nvfp4_per_token",
               "nv_quantize_nvfp4_per_token_grouped", "mx_dequantize", "nv_dequantize",
               "bsq_status_string", "bsq_abi_version"):
         assert n in names
@@ -96,6 +96,37 @@ def test_mx_quant_unused_copy_pointers_are_ignored(L):
     # rowwise only: the columnwise pointers may be anything, even misaligned
     assert mxq(L, mode=1, qc=3, sc=5, M=0) == bsq.BSQ_OK
     assert mxq(L, mode=1, qc=3, sc=5, K=48) == bsq.BSQ_ERR_SHAPE
+
+
+# ---------------------------------------------------------------------------------------
+# mx_quantize_mxfp8_grouped
+
+F_ = 0x7F000000
+
+
+def mxg(L, x=A, M=70, K=64, mode=2, off=E_, E=3, qr=B, sr=C, qc=D, sc=F_, s_ld=5, status=None):
+    return L.mx_quantize_mxfp8_grouped(x, M, K, mode, off, E, qr, sr, qc, sc, s_ld, status, None)
+
+
+def test_mx_grouped_validation(L):
+    assert mxg(L, mode=1) == bsq.BSQ_ERR_MODE                 # rowwise: the flat call
+    assert mxg(L, mode=0) == bsq.BSQ_ERR_MODE
+    assert mxg(L, K=48) == bsq.BSQ_ERR_SHAPE                  # K % 32
+    assert mxg(L, M=-1) == bsq.BSQ_ERR_SHAPE
+    assert mxg(L, E=0) == bsq.BSQ_ERR_SHAPE
+    assert mxg(L, s_ld=2) == bsq.BSQ_ERR_SHAPE                # fewer than ceil(70/32) = 3
+    assert mxg(L, M=2 ** 40, s_ld=2 ** 35) == bsq.BSQ_ERR_SHAPE   # 32-bit block indices
+    assert mxg(L, off=None) == bsq.BSQ_ERR_NULL
+    assert mxg(L, qc=None) == bsq.BSQ_ERR_NULL
+    assert mxg(L, mode=3, sr=None) == bsq.BSQ_ERR_NULL
+    assert mxg(L, off=E_ + 4) == bsq.BSQ_ERR_ALIGN
+    assert mxg(L, status=E_ + 0x1002) == bsq.BSQ_ERR_ALIGN
+    assert mxg(L, sc=F_ + 8) == bsq.BSQ_ERR_ALIGN
+    assert mxg(L, qc=A + 16) == bsq.BSQ_ERR_ALIAS              # output inside the input
+    assert mxg(L, off=F_ + 64) == bsq.BSQ_ERR_ALIAS            # offsets inside s_col
+    assert mxg(L, status=D + 8) == bsq.BSQ_ERR_ALIAS           # status inside q_col
+    assert mxg(L, M=0, s_ld=0) == bsq.BSQ_OK                   # no status asked: nothing to do
+    assert mxg(L, mode=2, qr=3, sr=5, M=0, s_ld=0) == bsq.BSQ_OK   # unused rowwise pointers
 
 
 # ---------------------------------------------------------------------------------------

@@ -141,3 +141,33 @@ def test_config5_layer_step_stream():
         i0 = torch.tensor([p[0] for p in pairs], device="cuda")
         i1 = torch.tensor([p[1] for p in pairs], device="cuda")
         assert torch.equal(q.index_select(0, i0), q.index_select(0, i1))
+
+
+def test_config5_routed_rows_mxfp8_grouped_by_expert():
+    """The layer step's 524288 routed rows as the MoE weight-gradient operand: MXFP8 with
+    32x1 blocks confined to each of the 128 expert segments (Zipf-routed, so nearly every
+    segment ends with a partial block), rowwise copy fused.  Compared on a seeded sample of
+    64 columns (a column's blocks depend on that column only) and 8192 rows."""
+    log("config5 grouped: generating")
+    cfg = workloads.config5()
+    a, tok, off = cfg["a"], cfg["token_idx"], cfg["offsets"]
+    xd = to_dev(a).index_select(0, torch.from_numpy(tok).cuda())
+    q_row, s_row, q_col, s_col, status = bsq.mx_quantize_mxfp8_grouped(
+        xd, torch.from_numpy(off).cuda(), "both")
+    torch.cuda.synchronize()
+    assert int(status.item()) == bsq.BSQ_OK
+    assert np.count_nonzero(np.diff(off) % 32) > 100           # partial blocks everywhere
+    del xd
+    log("config5 grouped: comparing sampled columns")
+    cols = np.sort(np.random.default_rng(56).choice(a.shape[1], 64, replace=False))
+    eq, es, ok = oracle.mx_quantize_colwise_grouped(np.ascontiguousarray(a[:, cols][tok]), off)
+    assert ok
+    cols_d = torch.from_numpy(cols).cuda()
+    assert_same("X q_col", bits(q_col.index_select(0, cols_d)), eq)
+    assert_same("X s_col", bits(s_col.index_select(0, cols_d))[:, :es.shape[1]], es)
+    log("config5 grouped: comparing sampled rows")
+    rows = np.sort(np.random.default_rng(57).choice(tok.size, 8192, replace=False))
+    er, esr = oracle.mx_quantize_rowwise(a[tok[rows]])
+    rows_d = torch.from_numpy(rows).cuda()
+    assert_same("X q_row", bits(q_row.index_select(0, rows_d)), er)
+    assert_same("X s_row", bits(s_row.index_select(0, rows_d)), esr)
