@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_mx_dequantize.argtypes = [P, P, I64, I64, P]
         L.oracle_nv_quantize_per_token.restype = None
         L.oracle_nv_quantize_per_token.argtypes = [P, I64, I64, P, P, P]
+        L.oracle_nv_quantize_per_group.restype = None
+        L.oracle_nv_quantize_per_group.argtypes = [P, I64, I64, P, I64, P, P, P]
         L.oracle_nv_dequantize.restype = None
         L.oracle_nv_dequantize.argtypes = [P, P, P, I64, I64, P]
         for name in ("oracle_enc_e4m3_array", "oracle_enc_e2m1_array", "oracle_rne_bf16_array"):
@@ -274,6 +276,27 @@ def nv_quantize_per_token_grouped(x: np.ndarray, offsets: np.ndarray):
               and np.all(np.diff(off) >= 0))
     q, sb, st = nv_quantize_per_token(x)
     return q, sb, st, ok
+
+
+def nv_quantize_per_group(x: np.ndarray, offsets):
+    """Standard NVFP4 with one FP32 scale per row group (a tensor, or an expert's tensor with
+    gate and up together): groups are row ranges offsets int64[G+1].  Returns (q[R][K/2],
+    sb[R][K/16], s_group[G] float32, ok); ok False (arrays None) for invalid offsets."""
+    x = _as_bf16_bits(x)
+    R, K = x.shape
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    ok = bool(off.ndim == 1 and off.size >= 2 and off[0] == 0 and off[-1] == R
+              and np.all(np.diff(off) >= 0))
+    if not ok:
+        return None, None, None, False
+    G = off.size - 1
+    q = np.empty((R, K // 2), np.uint8)
+    sb = np.empty((R, K // 16), np.uint8)
+    s = np.empty(G, np.float32)
+    lib().oracle_nv_quantize_per_group(_ptr(x), R, K, _ptr(off), G, _ptr(q), _ptr(sb), _ptr(s))
+    return q, sb, s, True
 
 
 def nv_dequantize(q: np.ndarray, sb: np.ndarray, st: np.ndarray) -> np.ndarray:

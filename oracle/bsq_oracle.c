@@ -320,39 +320,76 @@ float oracle_nv_block_multiplier(uint8_t sb, float s_t) {
     return (f > FLT_MAX) ? FLT_MAX : f;
 }
 
+/* Largest magnitude of n BF16 values (exact). */
+static double bf16_amax(const uint16_t* v, int64_t n) {
+    double amax = 0.0;
+    for (int64_t k = 0; k < n; ++k) {
+        double a = fabs(oracle_bf16_to_double(v[k]));
+        if (a > amax) amax = a;
+    }
+    return amax;
+}
+
+/* One row of K elements under the FP32 decode scale s: its K/16 block scales and K/2
+ * packed bytes. */
+static void nv_row(const uint16_t* xr, int64_t K, float s, uint8_t* qr, uint8_t* sbr) {
+    const int64_t nb = K / 16;
+    for (int64_t b = 0; b < nb; ++b) {
+        double amax_b = bf16_amax(xr + b * 16, 16);
+        uint8_t code_b = oracle_nv_block_scale((float)amax_b, s);
+        sbr[b] = code_b;
+        float f = oracle_nv_block_multiplier(code_b, s);
+        for (int i = 0; i < 16; i += 2) {
+            float x0 = (float)oracle_bf16_to_double(xr[b * 16 + i]);
+            float x1 = (float)oracle_bf16_to_double(xr[b * 16 + i + 1]);
+            uint8_t c0 = oracle_enc_e2m1((double)(x0 * f));  /* fl(x * f) */
+            uint8_t c1 = oracle_enc_e2m1((double)(x1 * f));
+            qr[(b * 16 + i) / 2] = (uint8_t)(c0 | (c1 << 4));
+        }
+    }
+}
+
 /* Per-token NVFP4 of x[R][K] (BF16 bits), K % 16 == 0.
  * q[R][K/2] packed E2M1 (element 2j low nibble), sb[R][K/16] E4M3, st[R] FP32. */
 void oracle_nv_quantize_per_token(const uint16_t* x, int64_t R, int64_t K,
                                   uint8_t* q, uint8_t* sb, float* st) {
     build_tables();
-    const int64_t nb = K / 16;
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < R; ++r) {
         const uint16_t* xr = x + r * K;
+        float s_t = oracle_nv_token_scale((float)bf16_amax(xr, K));   /* BF16 -> float exact */
+        st[r] = s_t;
+        nv_row(xr, K, s_t, q + r * (K / 2), sb + r * (K / 16));
+    }
+}
+
+/* Standard NVFP4 with one FP32 scale per group of rows: the two-level hierarchy with the
+ * coarse FP32 scale taken over a tensor instead of a token ("Format background": the
+ * scope of the FP32 scale is a recipe choice).  Groups are row ranges [off[g], off[g+1])
+ * -- a whole tensor, or an expert's tensor; an expert's gate and up projections go in one
+ * group so that both get the same scale ("Per-token activation scaling": gate and up
+ * share one FP32 scale in conversion and weight export).  The scale of group g is
+ * s_g = fl(amax_g / 2688) over all its elements (0 for an empty or all-zero group), and
+ * each of its rows is then encoded exactly as a per-token row with s_t = s_g.
+ * Offsets must be valid (off[0] = 0, non-decreasing, off[G] = R); the caller checks. */
+void oracle_nv_quantize_per_group(const uint16_t* x, int64_t R, int64_t K,
+                                  const int64_t* off, int64_t G,
+                                  uint8_t* q, uint8_t* sb, float* s_group) {
+    build_tables();
+    (void)R;
+    for (int64_t g = 0; g < G; ++g) {
         double amax = 0.0;
-        for (int64_t k = 0; k < K; ++k) {
-            double a = fabs(oracle_bf16_to_double(xr[k]));
+        for (int64_t r = off[g]; r < off[g + 1]; ++r) {
+            double a = bf16_amax(x + r * K, K);
             if (a > amax) amax = a;
         }
-        float s_t = oracle_nv_token_scale((float)amax);  /* BF16 -> float exact */
-        st[r] = s_t;
-        for (int64_t b = 0; b < nb; ++b) {
-            double amax_b = 0.0;
-            for (int i = 0; i < 16; ++i) {
-                double a = fabs(oracle_bf16_to_double(xr[b * 16 + i]));
-                if (a > amax_b) amax_b = a;
-            }
-            uint8_t code_b = oracle_nv_block_scale((float)amax_b, s_t);
-            sb[r * nb + b] = code_b;
-            float f = oracle_nv_block_multiplier(code_b, s_t);
-            for (int i = 0; i < 16; i += 2) {
-                float x0 = (float)oracle_bf16_to_double(xr[b * 16 + i]);
-                float x1 = (float)oracle_bf16_to_double(xr[b * 16 + i + 1]);
-                uint8_t c0 = oracle_enc_e2m1((double)(x0 * f));  /* fl(x * f) */
-                uint8_t c1 = oracle_enc_e2m1((double)(x1 * f));
-                q[r * (K / 2) + (b * 16 + i) / 2] = (uint8_t)(c0 | (c1 << 4));
-            }
-        }
+        s_group[g] = oracle_nv_token_scale((float)amax);
+    }
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t r = 0; r < off[G]; ++r) {
+        int64_t g = 0;
+        while (off[g + 1] <= r) ++g;                   /* the group of row r */
+        nv_row(x + r * K, K, s_group[g], q + r * (K / 2), sb + r * (K / 16));
     }
 }
 

@@ -258,3 +258,89 @@ def test_grouped_is_flat_and_checks_offsets():
     first = off.copy()
     first[0] = 1
     assert not oracle.nv_quantize_per_token_grouped(x, first)[3]
+
+
+# --------------------------------------------------------------------------- per-group scale
+
+def _golden(name):
+    out = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                k, *v = line.split()
+                out[k] = [int(t, 16) for t in v]
+    return out
+
+
+def _rand_rows(rng, R, K):
+    x = rng.integers(0, 1 << 16, size=(R, K), dtype=np.uint16)
+    x[(x & 0x7F80) == 0x7F80] &= 0xBFFF                        # finite only
+    return x
+
+
+def test_per_group_golden():
+    g = _golden("nvfp4_group_scale.txt")
+    x = np.array([g["x_row0"], g["x_row1"] * 16], np.uint16)
+    q, sb, s, ok = oracle.nv_quantize_per_group(x, [0, 2])
+    assert ok
+    assert s.view(np.uint32)[0] == g["group_scale_f32"][0]
+    assert sb[0, 0] == g["sb_row0"][0] and sb[1, 0] == g["sb_row1"][0]
+    assert q[0].tolist() == g["q_row0"] and np.all(q[1] == g["q_row1"][0])
+    y = oracle.nv_dequantize(q, sb, np.repeat(s, 2))
+    assert np.all(y[1] == g["dequant_row1"][0])
+    tq, tsb, tst = oracle.nv_quantize_per_token(x)
+    assert tsb[1, 0] == g["token_sb_row1"][0]
+    assert np.all(oracle.nv_dequantize(tq, tsb, tst)[1] == g["token_dequant_row1"][0])
+
+
+def test_per_group_with_one_row_per_group_is_per_token():
+    rng = np.random.default_rng(21)
+    x = _rand_rows(rng, 37, 96)
+    q, sb, s, ok = oracle.nv_quantize_per_group(x, np.arange(38))
+    tq, tsb, tst = oracle.nv_quantize_per_token(x)
+    assert ok
+    assert np.array_equal(q, tq) and np.array_equal(sb, tsb)
+    assert np.array_equal(s.view(np.uint32), tst.view(np.uint32))
+
+
+def test_per_group_scale_is_the_largest_token_scale_of_the_group():
+    """fl(a / 2688) is non-decreasing in a, so the scale of the group maximum is the
+    largest of the rows' per-token scales."""
+    rng = np.random.default_rng(22)
+    x = _rand_rows(rng, 60, 64)
+    x[10:20] = 0                                               # an all-zero group
+    off = [0, 10, 20, 20, 41, 60]                              # an empty group too
+    q, sb, s, ok = oracle.nv_quantize_per_group(x, off)
+    _, _, tst = oracle.nv_quantize_per_token(x)
+    assert ok
+    for g in range(len(off) - 1):
+        lo, hi = off[g], off[g + 1]
+        want = np.float32(0) if hi == lo else tst[lo:hi].max()
+        assert s[g] == want, g
+    assert s[1] == 0 and s[2] == 0
+
+
+def test_per_group_equals_per_token_when_every_row_holds_the_group_maximum():
+    """Put the group's largest magnitude into every row of the group: each row's own scale
+    is then the group's, so the bytes must equal the per-token bytes."""
+    rng = np.random.default_rng(23)
+    x = _rand_rows(rng, 50, 48)
+    off = [0, 7, 7, 30, 50]
+    for g in range(len(off) - 1):
+        lo, hi = off[g], off[g + 1]
+        if hi == lo:
+            continue
+        mags = x[lo:hi] & 0x7FFF
+        i, j = np.unravel_index(np.argmax(mags), mags.shape)
+        x[lo:hi, 5] = x[lo + i, j]
+    q, sb, s, ok = oracle.nv_quantize_per_group(x, off)
+    tq, tsb, tst = oracle.nv_quantize_per_token(x)
+    assert ok
+    assert np.array_equal(q, tq) and np.array_equal(sb, tsb)
+
+
+def test_per_group_rejects_bad_offsets():
+    x = np.zeros((8, 16), np.uint16)
+    for off in ([1, 8], [0, 5, 3, 8], [0, 7]):
+        assert oracle.nv_quantize_per_group(x, off)[3] is False
