@@ -310,11 +310,26 @@ def all_configs(torch, bsq, workloads, dev, reps=21):
         torch.from_numpy(c3["offsets"]).to(dev))
     del h
     c4 = workloads.config4()
-    for key in ("gate_up", "down"):
+    for key, rows in (("gate_up", 1536), ("down", 2048)):
         w = bf(c4[key])
         run(4, key, w, "nv")
         run(4, key, w, "mx_row")
-        del w
+        # standard NVFP4 export with one FP32 scale per expert tensor (gate and up share it):
+        # two passes over the weights, so x is read twice
+        M, K = w.shape
+        G = M // rows
+        off = torch.arange(0, M + 1, rows, dtype=torch.int64, device=dev)
+        g_out = (torch.empty(M, K // 2, dtype=torch.uint8, device=dev), torch.empty(M, K // 16, dtype=torch.uint8, device=dev),
+                 torch.empty(G, dtype=torch.float32, device=dev), torch.zeros(1, dtype=torch.int32, device=dev))
+        report(4, "nvfp4 per-expert-scale quant (two passes) " + key, "%dx%d" % (M, K),
+               4 * M * K + M * K // 2 + M * K // 16 + 4 * G, M * K,
+               lambda: bsq.nv_quantize_nvfp4_per_group(w, off, *g_out, stream=stream))
+        y = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+        report(4, "nvfp4 per-expert-scale dequant " + key, "%dx%d" % (M, K),
+               2 * M * K + M * K // 2 + M * K // 16 + 4 * G, M * K,
+               lambda: bsq.nv_dequantize_per_group(g_out[0], g_out[1], g_out[2], off, y, stream=stream))
+        torch.cuda.synchronize()
+        del w, g_out, y
     del c4
     c5 = workloads.config5()
     a, w = bf(c5["a"]), bf(c5["w"])

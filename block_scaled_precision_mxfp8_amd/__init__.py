@@ -12,6 +12,7 @@ Layouts (all row-major, all on the GPU):
   MXFP8 columnwise  q_col u8 [K, M]      s_col u8 [K, M/32]   (stored transposed)
   MXFP8 grouped     q_col u8 [K, M]      s_col u8 [K, s_ld]   (32x1 blocks per expert)
   NVFP4 per token   q u8 [R, K/2]        sb u8 [R, K/16]      st f32 [R]
+  NVFP4 per group   q u8 [R, K/2]        sb u8 [R, K/16]      s_group f32 [G]
 BF16 tensors are ``torch.bfloat16``.
 """
 from __future__ import annotations
@@ -69,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.nv_quantize_nvfp4_per_token_grouped.argtypes = [P, I64, I64, P, I64, P, P, P, P, P]
         L.mx_quantize_mxfp8_grouped.restype = I32
         L.mx_quantize_mxfp8_grouped.argtypes = [P, I64, I64, I32, P, I64, P, P, P, P, I64, P, P]
+        L.nv_quantize_nvfp4_per_group.restype = I32
+        L.nv_quantize_nvfp4_per_group.argtypes = [P, I64, I64, P, I64, P, P, P, P, P]
+        L.nv_dequantize_per_group.restype = I32
+        L.nv_dequantize_per_group.argtypes = [P, P, P, P, I64, I64, I64, P, P]
         L.mx_dequantize.restype = I32
         L.mx_dequantize.argtypes = [P, P, I64, I64, P, P]
         L.nv_dequantize.restype = I32
@@ -274,3 +279,50 @@ __all__ = [
     "mx_dequantize", "nv_dequantize", "status_string", "abi_version", "lib", "BsqError",
     "MX_ROWWISE", "MX_COLWISE", "MX_BOTH",
 ]
+
+
+def nv_quantize_nvfp4_per_group(x: torch.Tensor, group_offsets: torch.Tensor, q=None, sb=None,
+                                s_group=None, status=None, stream=None):
+    """Standard NVFP4 of x [R, K] bf16 with one FP32 scale per row group (group_offsets
+    int64 [G+1] on the GPU; put an expert's gate and up rows in one group).  Returns
+    (q [R, K/2], sb [R, K/16], s_group [G] f32, status); status is a device int32 [1] the
+    kernel sets to BSQ_OK or BSQ_ERR_OFFSETS (read it after synchronising)."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    R, K = x.shape
+    _dev_tensor(x, "x", torch.bfloat16, (R, K))
+    if group_offsets.dim() != 1 or group_offsets.numel() < 2:
+        raise ValueError("group_offsets must be int64 [G+1] with G >= 1")
+    G = group_offsets.numel() - 1
+    _dev_tensor(group_offsets, "group_offsets", torch.int64, (G + 1,))
+    if K % 16:
+        raise ValueError("NVFP4 needs K % 16 == 0")
+    q = _out(q, "q", torch.uint8, (R, K // 2), x)
+    sb = _out(sb, "sb", torch.uint8, (R, K // 16), x)
+    s_group = _out(s_group, "s_group", torch.float32, (G,), x)
+    status = _out(status, "status", torch.int32, (1,), x)
+    _check("nv_quantize_nvfp4_per_group",
+           lib().nv_quantize_nvfp4_per_group(_ptr(x), R, K, _ptr(group_offsets), G, _ptr(q), _ptr(sb),
+                                             _ptr(s_group), _ptr(status), _stream(stream)))
+    return q, sb, s_group, status
+
+
+def nv_dequantize_per_group(q: torch.Tensor, sb: torch.Tensor, s_group: torch.Tensor,
+                            group_offsets: torch.Tensor, y=None, stream=None) -> torch.Tensor:
+    """BF16 [R, K] from NVFP4 with one FP32 scale per row group."""
+    if q.dim() != 2:
+        raise ValueError("q must be 2-D")
+    R, half = q.shape
+    K = 2 * half
+    _dev_tensor(q, "q", torch.uint8, (R, half))
+    if K % 16:
+        raise ValueError("NVFP4 needs K % 16 == 0")
+    G = group_offsets.numel() - 1
+    _dev_tensor(group_offsets, "group_offsets", torch.int64, (G + 1,))
+    _dev_tensor(sb, "sb", torch.uint8, (R, K // 16))
+    _dev_tensor(s_group, "s_group", torch.float32, (G,))
+    y = _out(y, "y", torch.bfloat16, (R, K), q)
+    _check("nv_dequantize_per_group",
+           lib().nv_dequantize_per_group(_ptr(q), _ptr(sb), _ptr(s_group), _ptr(group_offsets), G, R, K,
+                                         _ptr(y), _stream(stream)))
+    return y

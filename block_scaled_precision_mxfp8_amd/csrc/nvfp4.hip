@@ -131,36 +131,45 @@ __device__ __forceinline__ void load_span(uint4 (&v)[NS], const uint4* __restric
     }
 }
 
-// Quantize the span held in v (all lanes of the wave take part): rows r0 .. r0+RPW-1,
-// n_ch valid chunks.  The span's block-scale bytes are gathered in the wave's LDS slice
-// `lsb` (32 NS bytes) and leave as 16-byte stores when the run is 16-byte aligned.
+// Largest magnitudes of the span's rows (BF16 bits; row a in the low half, row b in the
+// high half for RPW = 2), uniform over the wave.
+template <int NS, int RPW>
+__device__ __forceinline__ uint32_t span_amax(const uint4 (&v)[NS], int cpr) {
+    static_assert(RPW == 1 || RPW == 2, "one or two rows per wave");
+    const int lane = threadIdx.x & 63;
+    uint32_t m = 0u;
+    if (RPW == 1) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) m = max(m, chunk_absmax8(v[j]));
+        return wave_max(m);
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const uint32_t c = chunk_absmax8(v[j]);
+        m = pk_max_u16(m, (64 * j + lane >= cpr) ? (c << 16) : c);
+    }
+    return wave_max_pk(m);
+}
+
+// FP32 decode scale of a row or group from its largest magnitude (BF16 bits):
+// fl(amax / (6 * 448)).
+__device__ __forceinline__ float nv_decode_scale(uint32_t amax_bf16) {
+    return __uint_as_float(amax_bf16 << 16) / 2688.0f;
+}
+
+// Quantize the span held in v (all lanes of the wave take part) under the FP32 decode
+// scales s_a (row r0) and s_b (row r0+1, RPW = 2): n_ch valid chunks.  The span's
+// block-scale bytes are gathered in the wave's LDS slice `lsb` (32 NS bytes) and leave
+// as 16-byte stores when the run is 16-byte aligned.
 template <int NS, int RPW, bool FULL>
 __device__ __forceinline__ void quant_span(const uint4 (&v)[NS], int64_t r0, int n_ch, int cpr,
+                                           float s_a, float s_b,
                                            uint32_t* __restrict__ q, uint8_t* __restrict__ sb,
-                                           float* __restrict__ st, uint8_t* lsb) {
-    static_assert(RPW == 1 || RPW == 2, "one or two rows per wave");
+                                           uint8_t* lsb) {
     const int lane = threadIdx.x & 63;
     // second row of the span for slot j? (RPW == 2 only; cpr is the row length in chunks)
     auto in_b = [&](int j) { return RPW == 2 && 64 * j + lane >= cpr; };
-
-    float s_a, s_b = 0.0f;
-    if (RPW == 1) {
-        uint32_t m = 0u;
-#pragma unroll
-        for (int j = 0; j < NS; ++j) m = max(m, chunk_absmax8(v[j]));
-        s_a = __uint_as_float(wave_max(m) << 16) / 2688.0f;          // fl(amax / (6 * 448))
-    } else {
-        uint32_t m = 0u;                                              // row a low, row b high
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            const uint32_t c = chunk_absmax8(v[j]);
-            m = pk_max_u16(m, in_b(j) ? (c << 16) : c);
-        }
-        const uint32_t mm = wave_max_pk(m);
-        s_a = __uint_as_float(mm << 16) / 2688.0f;
-        s_b = __uint_as_float(mm & 0xFFFF0000u) / 2688.0f;
-    }
-    const float p_a = 6.0f * s_a, p_b = 6.0f * s_b;                   // fl(6 s_t)
+    const float p_a = 6.0f * s_a, p_b = 6.0f * s_b;                   // fl(6 s)
 
     uint32_t* qs = q + r0 * cpr;                      // 4 bytes of q per chunk
     uint8_t* sbs = sb + r0 * (cpr >> 1);              // one scale byte per chunk pair
@@ -199,8 +208,6 @@ __device__ __forceinline__ void quant_span(const uint4 (&v)[NS], int64_t r0, int
             if (!odd) lsb[32 * (j + 1) + (lane >> 1)] = (uint8_t)code1;
         }
     }
-    if (lane == 0) st[r0] = s_a;
-    if (RPW == 2 && lane == 1 && n_ch > cpr) st[r0 + 1] = s_b;
     // the wave's LDS slice: written above by even lanes, read below by the first lanes
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -214,7 +221,7 @@ __device__ __forceinline__ void quant_span(const uint4 (&v)[NS], int64_t r0, int
     }
 }
 
-// One span per wave.
+// One span per wave, per-token scales.
 template <int NS, int RPW, bool FULL>
 __global__ __launch_bounds__(64 * NV_WAVES)
 void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
@@ -223,6 +230,7 @@ void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
                           const int64_t* __restrict__ offsets, int64_t E,
                           int32_t* __restrict__ status) {
     const int wave = wave_id();
+    const int lane = threadIdx.x & 63;
     if (status != nullptr && blockIdx.x == 0 && wave == 0) check_offsets(offsets, E, R, status);
     const int64_t r0 = ((int64_t)blockIdx.x * NV_WAVES + wave) * RPW;
     if (r0 >= R) return;
@@ -231,7 +239,131 @@ void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
     const int n_ch = (RPW == 2 && r0 + 1 >= R) ? cpr : RPW * cpr;
     uint4 v[NS];
     load_span<NS, FULL>(v, x + r0 * cpr, n_ch);
-    quant_span<NS, RPW, FULL>(v, r0, n_ch, cpr, q, sb, st, lds_sb[wave]);
+    const uint32_t mm = span_amax<NS, RPW>(v, cpr);
+    const float s_a = nv_decode_scale(mm & 0xFFFFu);
+    const float s_b = nv_decode_scale(mm >> 16);
+    quant_span<NS, RPW, FULL>(v, r0, n_ch, cpr, s_a, s_b, q, sb, lds_sb[wave]);
+    if (lane == 0) st[r0] = s_a;
+    if (RPW == 2 && lane == 1 && n_ch > cpr) st[r0 + 1] = s_b;
+}
+
+// ----------------------------------------------------------------------------- per group
+
+// Standard NVFP4 with one FP32 scale per group of rows (a tensor, or an expert's tensor
+// with its gate and up projections together).  Page "Towards Blackwell-native 8-bit and
+// 4-bit RL", section "Format background": the scope of the coarse FP32 scale is a recipe
+// choice; section "Per-token activation scaling": gate and up share one FP32 scale in
+// conversion and weight export.  s_g = fl(amax_g / 2688) over the group, then every row
+// is encoded as a per-token row with s_t = s_g.  The group maximum needs the whole group
+// before any element is encoded, so this takes two passes over x: the maxima are
+// accumulated with atomicMax on their binary32 bit patterns (non-negative, so unsigned
+// order is value order) in the caller's s_group array itself, which the last launch turns
+// into the scales in place.
+
+// Group offsets staged in LDS for the row -> group lookup (larger G searches in HBM).
+constexpr int NV_GROUP_LDS = 1024;
+
+// Group of row r: the g in [0, G) with off[g] <= r < off[g+1] (clamped into [0, G) so
+// that invalid offsets still index inside s_group).
+__device__ __forceinline__ int64_t group_of(int64_t r, const int64_t* off, int64_t G) {
+    int64_t lo = 0, hi = G;                           // off[lo] <= r < off[hi] (if valid)
+    while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (off[mid] <= r) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// The workgroup's view of the offsets: the LDS copy when it fits, else the global array.
+__device__ __forceinline__ const int64_t* stage_offsets(const int64_t* __restrict__ off, int64_t G,
+                                                        int64_t* lds_off) {
+    if (G + 1 > NV_GROUP_LDS) return off;
+    for (int64_t i = threadIdx.x; i <= G; i += 64 * NV_WAVES) lds_off[i] = off[i];
+    __syncthreads();
+    return lds_off;
+}
+
+__global__ __launch_bounds__(256)
+void nv_group_init_kernel(uint32_t* __restrict__ amax_bits, int64_t G, const int64_t* __restrict__ off,
+                          int64_t R, int32_t* __restrict__ status) {
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (g < G) amax_bits[g] = 0u;
+    if (status != nullptr && blockIdx.x == 0 && threadIdx.x < 64) check_offsets(off, G, R, status);
+}
+
+// Pass 1: group maxima.  Each wave streams a contiguous range of rows as one flat run of
+// 16-byte chunks per group segment (rows end on chunk boundaries), keeps a lane-local
+// running maximum, and folds it into the group's maximum with one wave reduction and one
+// atomic per segment -- a few atomics per group instead of one per row.  Ordinary loads:
+// the quantize pass walks the tensor backwards and finds the last rows read here still
+// in the Infinity Cache.
+constexpr int NV_AMAX_UNROLL = 4;
+
+__global__ __launch_bounds__(64 * NV_WAVES)
+void nv_group_amax_kernel(const uint4* __restrict__ x, int64_t R, int64_t K,
+                          const int64_t* __restrict__ off, int64_t G, uint32_t* __restrict__ amax_bits,
+                          int64_t rows_per_wave) {
+    __shared__ int64_t lds_off[NV_GROUP_LDS];
+    const int64_t* offs = stage_offsets(off, G, lds_off);
+    const int lane = threadIdx.x & 63;
+    const int64_t w = (int64_t)blockIdx.x * NV_WAVES + wave_id();
+    int64_t r = w * rows_per_wave;
+    const int64_t r_end = min(R, r + rows_per_wave);
+    if (r >= r_end) return;
+    const int64_t cpr = K >> 3;
+    int64_t g = group_of(r, offs, G);
+    while (r < r_end) {
+        // rows r .. seg_end-1 lie in group g (clamped for invalid offsets)
+        int64_t seg_end = (g + 1 <= G) ? offs[g + 1] : r_end;
+        if (seg_end > r_end || g == G - 1) seg_end = r_end;
+        if (seg_end <= r) seg_end = r + 1;
+        const uint4* p = x + r * cpr;
+        const int64_t n = (seg_end - r) * cpr;
+        uint32_t m = 0u;
+        int64_t c = lane;
+        for (; c + 64 * (NV_AMAX_UNROLL - 1) < n; c += 64 * NV_AMAX_UNROLL) {
+            uint4 v[NV_AMAX_UNROLL];
+#pragma unroll
+            for (int u = 0; u < NV_AMAX_UNROLL; ++u) v[u] = p[c + 64 * u];
+#pragma unroll
+            for (int u = 0; u < NV_AMAX_UNROLL; ++u) m = max(m, chunk_absmax8(v[u]));
+        }
+        for (; c < n; c += 64) m = max(m, chunk_absmax8(p[c]));
+        m = wave_max(m);
+        if (lane == 0) atomicMax(amax_bits + g, m << 16);
+        r = seg_end;
+        if (r < r_end) g = group_of(r, offs, G);
+    }
+}
+
+// Pass 2: quantize every span under its rows' group scales.
+template <int NS, int RPW, bool FULL>
+__global__ __launch_bounds__(64 * NV_WAVES)
+void nv_group_quant_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q, uint8_t* __restrict__ sb,
+                           int64_t R, int64_t K, const int64_t* __restrict__ off, int64_t G,
+                           const uint32_t* __restrict__ amax_bits) {
+    __shared__ int64_t lds_off[NV_GROUP_LDS];
+    __shared__ __align__(16) uint8_t lds_sb[NV_WAVES][32 * NS];
+    const int wave = wave_id();
+    // workgroups in reverse row order: the first spans read are the rows the maximum pass
+    // read last, still in the Infinity Cache when the tensor is not much larger than it
+    const int64_t wg = (int64_t)gridDim.x - 1 - blockIdx.x;
+    const int64_t r0 = (wg * NV_WAVES + wave) * RPW;
+    const int cpr = (int)(K >> 3);
+    const int n_ch = r0 >= R ? 0 : (RPW == 2 && r0 + 1 >= R) ? cpr : RPW * cpr;
+    uint4 v[NS];
+    if (n_ch > 0) load_span<NS, FULL>(v, x + r0 * cpr, n_ch);
+    const int64_t* offs = stage_offsets(off, G, lds_off);
+    if (n_ch == 0) return;
+    const float s_a = nv_decode_scale(amax_bits[group_of(r0, offs, G)] >> 16);
+    const float s_b = (RPW == 2 && n_ch > cpr) ? nv_decode_scale(amax_bits[group_of(r0 + 1, offs, G)] >> 16) : 0.0f;
+    quant_span<NS, RPW, FULL>(v, r0, n_ch, cpr, s_a, s_b, q, sb, lds_sb[wave]);
+}
+
+__global__ __launch_bounds__(256)
+void nv_group_finalize_kernel(float* __restrict__ s_group, int64_t G) {
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (g < G) s_group[g] = nv_decode_scale(__float_as_uint(s_group[g]) >> 16);
 }
 
 // Rows longer than the register-resident variants: two passes over the row (the second
@@ -274,6 +406,37 @@ void nv_quant_rows_long_kernel(const uint4* __restrict__ x, uint32_t* __restrict
     if (lane == 0) st[row] = s_t;
 }
 
+// Quantize pass for rows longer than the register-resident variants (one wave per row,
+// the row streamed twice; same arithmetic).
+__global__ __launch_bounds__(64 * NV_WAVES)
+void nv_group_quant_long_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q, uint8_t* __restrict__ sb,
+                                int64_t R, int64_t K, const int64_t* __restrict__ off, int64_t G,
+                                const uint32_t* __restrict__ amax_bits) {
+    __shared__ int64_t lds_off[NV_GROUP_LDS];
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * NV_WAVES + (threadIdx.x >> 6);
+    const int64_t* offs = stage_offsets(off, G, lds_off);
+    if (row >= R) return;
+    const int64_t cpr = K >> 3;
+    const uint4* xr = x + row * cpr;
+    const float s = nv_decode_scale(amax_bits[group_of(row, offs, G)] >> 16);
+    const float p = 6.0f * s;
+    uint32_t* qr = q + row * cpr;
+    uint8_t* sbr = sb + row * (K >> 4);
+    for (int64_t base = 0; base < cpr; base += 64) {
+        const int64_t ch = base + lane;
+        const uint4 v = (ch < cpr) ? xr[ch] : make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t amax_b = pair_max(chunk_absmax8(v));
+        float f;
+        const uint32_t code = nv_block_scale(amax_b, s, p, f);
+        const uint32_t packed = nv_enc8(v, f);
+        if (ch < cpr) {
+            qr[ch] = packed;
+            if ((lane & 1) == 0) sbr[ch >> 1] = (uint8_t)code;
+        }
+    }
+}
+
 // ----------------------------------------------------------------------------- dequant
 
 // NVFP4 -> BF16, a 1-D stream over half blocks (8 elements = 4 bytes of q = 16 bytes of
@@ -303,11 +466,17 @@ __device__ __forceinline__ uint32_t nv_dec2_nan(uint32_t word, float bscale, flo
     return lo | hi;
 }
 
-template <int NVDQ_SLOTS>
+// GROUPED: st holds one scale per row group (offsets off[0..G], rows counted from row0);
+// each row's scale is that of its group.
+template <int NVDQ_SLOTS, bool GROUPED>
 __global__ __launch_bounds__(256)
 void nv_dequant_kernel(const uint32_t* __restrict__ q, const uint8_t* __restrict__ sb,
                        const float* __restrict__ st, uint4* __restrict__ y,
-                       uint32_t n_half, FastDiv halves_per_row) {
+                       uint32_t n_half, FastDiv halves_per_row,
+                       const int64_t* __restrict__ off, int64_t G, int64_t row0) {
+    __shared__ int64_t lds_off[GROUPED ? NV_GROUP_LDS : 1];
+    const int64_t* offs = GROUPED ? stage_offsets(off, G, lds_off) : nullptr;
+    const int64_t g_first = GROUPED ? group_of(row0 + fastdiv(blockIdx.x * (256u * NVDQ_SLOTS), halves_per_row), offs, G) : 0;
     const uint32_t base = blockIdx.x * (256u * NVDQ_SLOTS) + threadIdx.x;
     uint32_t w[NVDQ_SLOTS], code[NVDQ_SLOTS];
     float s_t[NVDQ_SLOTS];
@@ -317,7 +486,14 @@ void nv_dequant_kernel(const uint32_t* __restrict__ q, const uint8_t* __restrict
         const bool ok = h < n_half;
         w[j] = ok ? ld_stream<NVDQ_NT_LOAD>(q + h) : 0u;
         code[j] = ok ? sb[h >> 1] : 0u;
-        s_t[j] = ok ? st[fastdiv(h, halves_per_row)] : 0.0f;
+        if (GROUPED) {
+            // rows of one workgroup span a few rows: walk from the group of its first row
+            const int64_t r = row0 + fastdiv(h, halves_per_row);
+            int64_t g = g_first;
+            while (g + 1 < G && offs[g + 1] <= r) ++g;
+            s_t[j] = ok ? st[g] : 0.0f;
+        }
+        else s_t[j] = ok ? st[fastdiv(h, halves_per_row)] : 0.0f;
     }
 #pragma unroll
     for (int j = 0; j < NVDQ_SLOTS; ++j) {
@@ -399,9 +575,10 @@ hipError_t launch_nv_quant(const void* x, int64_t R, int64_t K, void* q, void* s
     return hipGetLastError();
 }
 
-template <int SLOTS>
+template <int SLOTS, bool GROUPED>
 static hipError_t launch_nv_dequant_slots(const void* q, const void* sb, const float* st, int64_t R,
-                                          int64_t K, void* y, hipStream_t stream) {
+                                          int64_t K, void* y, const int64_t* off, int64_t G,
+                                          hipStream_t stream) {
     // 32-bit half-block indices: launch row ranges of fewer than 2^31 half blocks each
     const int64_t hpr = K / 8;
     const int64_t rows_per_launch = ((int64_t)1 << 31) / hpr;
@@ -410,9 +587,10 @@ static hipError_t launch_nv_dequant_slots(const void* q, const void* sb, const f
         const int64_t rows = (R - r0 < rows_per_launch) ? R - r0 : rows_per_launch;
         const int64_t n_half = rows * hpr;
         const int64_t grid = (n_half + 256 * SLOTS - 1) / (256 * SLOTS);
-        hipLaunchKernelGGL(nv_dequant_kernel<SLOTS>, dim3((unsigned)grid), dim3(256), 0, stream,
+        hipLaunchKernelGGL((nv_dequant_kernel<SLOTS, GROUPED>), dim3((unsigned)grid), dim3(256), 0, stream,
                            (const uint32_t*)q + r0 * hpr, (const uint8_t*)sb + r0 * (K / 16),
-                           st + r0, (uint4*)y + r0 * hpr, (uint32_t)n_half, div);
+                           GROUPED ? st : st + r0, (uint4*)y + r0 * hpr, (uint32_t)n_half, div,
+                           off, G, r0);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -421,7 +599,69 @@ static hipError_t launch_nv_dequant_slots(const void* q, const void* sb, const f
 
 hipError_t launch_nv_dequant(const void* q, const void* sb, const float* st, int64_t R, int64_t K,
                              void* y, hipStream_t stream) {
-    return launch_nv_dequant_slots<NV_DQ_SLOTS>(q, sb, st, R, K, y, stream);
+    return launch_nv_dequant_slots<NV_DQ_SLOTS, false>(q, sb, st, R, K, y, nullptr, 0, stream);
+}
+
+// Slots per thread of the per-group dequant: each workgroup stages the offsets and finds
+// the group of its first row, so it takes more data than the per-token one.
+#ifndef BSQ_NV_DQ_GROUP_SLOTS
+#define BSQ_NV_DQ_GROUP_SLOTS 8
+#endif
+
+hipError_t launch_nv_dequant_group(const void* q, const void* sb, const float* s_group, const int64_t* off,
+                                   int64_t G, int64_t R, int64_t K, void* y, hipStream_t stream) {
+    return launch_nv_dequant_slots<BSQ_NV_DQ_GROUP_SLOTS, true>(q, sb, s_group, R, K, y, off, G, stream);
+}
+
+template <int NS, int RPW>
+static void launch_group_passes(const void* x, int64_t R, int64_t K, void* q, void* sb, uint32_t* bits,
+                                const int64_t* off, int64_t G, hipStream_t stream) {
+    const int64_t spans = (R + RPW - 1) / RPW;
+    const int64_t grid = (spans + NV_WAVES - 1) / NV_WAVES;
+    const bool full = RPW * K == 512 * NS && R % RPW == 0;
+    if (full)
+        hipLaunchKernelGGL((nv_group_quant_kernel<NS, RPW, true>), dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
+                           stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, R, K, off, G, bits);
+    else
+        hipLaunchKernelGGL((nv_group_quant_kernel<NS, RPW, false>), dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
+                           stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, R, K, off, G, bits);
+}
+
+hipError_t launch_nv_quant_group(const void* x, int64_t R, int64_t K, const int64_t* off, int64_t G,
+                                 void* q, void* sb, float* s_group, int32_t* status, hipStream_t stream) {
+    uint32_t* bits = reinterpret_cast<uint32_t*>(s_group);   // group maxima, then the scales
+    const unsigned gg = (unsigned)((G + 255) / 256);
+    hipLaunchKernelGGL(nv_group_init_kernel, dim3(gg), dim3(256), 0, stream, bits, G, off, R, status);
+    if (R > 0 && K > 0) {
+        // pass 1: about 8 waves per compute unit, each over a contiguous range of rows
+        const int64_t waves = 256 * 8 * NV_WAVES;
+        const int64_t rpw = (R + waves - 1) / waves;
+        const int64_t agrid = ((R + rpw - 1) / rpw + NV_WAVES - 1) / NV_WAVES;
+        hipLaunchKernelGGL(nv_group_amax_kernel, dim3((unsigned)agrid), dim3(64 * NV_WAVES), 0, stream,
+                           (const uint4*)x, R, K, off, G, bits, rpw);
+        if (K <= NV_PAIR_MAX_K) {
+            switch ((2 * (K / 8) + 63) / 64) {
+                case 1: launch_group_passes<1, 2>(x, R, K, q, sb, bits, off, G, stream); break;
+                case 2: launch_group_passes<2, 2>(x, R, K, q, sb, bits, off, G, stream); break;
+                default: launch_group_passes<3, 2>(x, R, K, q, sb, bits, off, G, stream); break;
+            }
+        } else {
+            switch ((K / 8 + 63) / 64) {
+                case 2: launch_group_passes<2, 1>(x, R, K, q, sb, bits, off, G, stream); break;
+                case 3: launch_group_passes<3, 1>(x, R, K, q, sb, bits, off, G, stream); break;
+                case 4: launch_group_passes<4, 1>(x, R, K, q, sb, bits, off, G, stream); break;
+                case 5: case 6: launch_group_passes<6, 1>(x, R, K, q, sb, bits, off, G, stream); break;
+                case 7: case 8: launch_group_passes<8, 1>(x, R, K, q, sb, bits, off, G, stream); break;
+                default: {
+                    const int64_t grid = (R + NV_WAVES - 1) / NV_WAVES;
+                    hipLaunchKernelGGL(nv_group_quant_long_kernel, dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
+                                       stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, R, K, off, G, bits);
+                }
+            }
+        }
+    }
+    hipLaunchKernelGGL(nv_group_finalize_kernel, dim3(gg), dim3(256), 0, stream, s_group, G);
+    return hipGetLastError();
 }
 
 }  // namespace bsq

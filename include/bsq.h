@@ -144,6 +144,40 @@ int mx_quantize_mxfp8_grouped(const void* x_bf16, int64_t M, int64_t K, int mode
                               int32_t* status_dev, void* stream);
 
 /*
+ * Standard NVFP4 of x[R][K] (BF16) with one FP32 scale per group of rows: rows
+ * [offsets[g], offsets[g+1]) form group g (a whole tensor, or one expert's tensor; an
+ * expert's gate and up projections belong in one group).
+ * Passages: "Format background" (the coarse FP32 scale maps a tensor or a token into the
+ * NVFP4 range; its scope is a recipe choice) and "Per-token activation scaling" (gate and
+ * up share one FP32 scale in conversion and live weight export).
+ * Per group: s_g = fl(amax_g / 2688) over all its elements (0 for an empty group); every
+ * row of the group is then encoded with the per-token steps under s_t = s_g.
+ * Needs K % 16 == 0.  Outputs:  q u8 [R][K/2],  sb u8 [R][K/16] (as per-token), and
+ * s_group f32 [G] (DEVICE).  The group maximum needs the whole group before any element
+ * can be encoded, so x is read twice (two passes); s_group also holds the group maxima
+ * between the passes (four launches on `stream`).
+ * group_offsets: DEVICE int64 [G+1], G >= 1, checked on the device: if status_dev is not
+ * NULL the kernel writes BSQ_ERR_OFFSETS when offsets[0] != 0, offsets[G] != R or the
+ * offsets decrease, BSQ_OK otherwise.  With invalid offsets the output bytes are
+ * unspecified, but nothing outside the given buffers is written.
+ */
+int nv_quantize_nvfp4_per_group(const void* x_bf16, int64_t R, int64_t K,
+                                const int64_t* group_offsets, int64_t G,
+                                void* q, void* sb, float* s_group,
+                                int32_t* status_dev, void* stream);
+
+/*
+ * BF16 [R][K] from NVFP4 with one FP32 scale per group of rows (the output of
+ * nv_quantize_nvfp4_per_group): y = RNE_BF16(fl(exact(DEC_E2M1(q) * DEC_E4M3(sb)) * s_g))
+ * for the group g of the row; a NaN result is 0x7FC0.  Passage: "High-precision and
+ * dequantized backward".  Needs K % 16 == 0; s_group and group_offsets are DEVICE arrays
+ * [G] and [G+1] (valid offsets assumed).
+ */
+int nv_dequantize_per_group(const void* q, const void* sb, const float* s_group,
+                            const int64_t* group_offsets, int64_t G, int64_t R, int64_t K,
+                            void* y_bf16, void* stream);
+
+/*
  * MXFP8 dequantization to BF16, in the stored layout: q u8 [rows][cols] E4M3 and
  * s u8 [rows][cols/32] E8M0 (blocks of 32 along the stored last dimension).
  * Passage: "High-precision and dequantized backward" (backward GEMMs consume BF16

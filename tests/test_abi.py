@@ -41,7 +41,8 @@ def _declared_functions():
 
 def test_header_declares_the_expected_entry_points():
     names = _declared_functions()
-    for n in ("mx_quantize_mxfp8", "mx_quantize_mxfp8_grouped", "nv_quantize_nvfp4_per_token",
+    for n in ("mx_quantize_mxfp8", "mx_quantize_mxfp8_grouped", "nv_quantize_nvfp4_per_group",
+              "nv_dequantize_per_group", "nv_quantize_nvfp4_per_token",
               "nv_quantize_nvfp4_per_token_grouped", "mx_dequantize", "nv_dequantize",
               "bsq_status_string", "bsq_abi_version"):
         assert n in names
@@ -162,6 +163,31 @@ def test_nv_grouped_validation(L):
     assert nvg(L, status=B) == bsq.BSQ_ERR_ALIAS               # status inside q
     assert nvg(L, K=40) == bsq.BSQ_ERR_SHAPE
     assert nvg(L, R=0) == bsq.BSQ_OK                           # no status asked: nothing to do
+
+
+def nvpg(L, x=A, R=4, K=64, off=E_, G=2, q=B, sb=C, s=D, status=None):
+    return L.nv_quantize_nvfp4_per_group(x, R, K, off, G, q, sb, s, status, None)
+
+
+def test_nv_per_group_validation(L):
+    assert nvpg(L, K=40) == bsq.BSQ_ERR_SHAPE
+    assert nvpg(L, R=-2) == bsq.BSQ_ERR_SHAPE
+    assert nvpg(L, G=0) == bsq.BSQ_ERR_SHAPE
+    assert nvpg(L, off=None) == bsq.BSQ_ERR_NULL
+    assert nvpg(L, s=None) == bsq.BSQ_ERR_NULL
+    assert nvpg(L, q=None) == bsq.BSQ_ERR_NULL
+    assert nvpg(L, off=E_ + 4) == bsq.BSQ_ERR_ALIGN
+    assert nvpg(L, s=D + 4) == bsq.BSQ_ERR_ALIGN
+    assert nvpg(L, status=E_ + 0x1002) == bsq.BSQ_ERR_ALIGN
+    assert nvpg(L, s=A + 16) == bsq.BSQ_ERR_ALIAS              # scales inside the input
+    assert nvpg(L, off=C) == bsq.BSQ_ERR_ALIAS                 # offsets inside sb
+    f = L.nv_dequantize_per_group
+    assert f(A, B, C, D, 2, 4, 40, E_, None) == bsq.BSQ_ERR_SHAPE
+    assert f(A, B, C, D, 0, 4, 64, E_, None) == bsq.BSQ_ERR_SHAPE
+    assert f(A, B, None, D, 2, 4, 64, E_, None) == bsq.BSQ_ERR_NULL
+    assert f(A, B, C, D + 4, 2, 4, 64, E_, None) == bsq.BSQ_ERR_ALIGN
+    assert f(A, B, C, D, 2, 4, 64, A + 16, None) == bsq.BSQ_ERR_ALIAS
+    assert f(A, B, C, D, 2, 0, 64, E_, None) == bsq.BSQ_OK
 
 
 # ---------------------------------------------------------------------------------------

@@ -84,6 +84,31 @@ def test_config4_weight_export_128_experts():
         del wd
 
 
+def test_config4_weight_export_one_scale_per_expert():
+    """Standard NVFP4 export of the 128 experts with one FP32 scale per expert tensor: the
+    fused gate/up projection of an expert is one group (1536 rows, gate and up sharing one
+    scale), the down projection another (2048 rows).  Every output byte is compared."""
+    log("config4 per-expert scale: generating")
+    cfg = workloads.config4()
+    for key, rows in (("gate_up", 1536), ("down", 2048)):
+        w = cfg[key]
+        off = np.arange(0, w.shape[0] + 1, rows, dtype=np.int64)
+        assert off[-1] == w.shape[0] and off.size == 129
+        offd = torch.from_numpy(off).cuda()
+        log("config4 %s: nvfp4 per expert" % key)
+        q, sb, s, status = bsq.nv_quantize_nvfp4_per_group(to_dev(w), offd)
+        y = bsq.nv_dequantize_per_group(q, sb, s, offd)
+        torch.cuda.synchronize()
+        assert int(status.item()) == bsq.BSQ_OK
+        eq, esb, es, ok = oracle.nv_quantize_per_group(w, off)
+        assert ok
+        assert_same(key + " s_group", bits(s), es.view(np.uint32))
+        assert_same(key + " sb", bits(sb), esb)
+        assert_same(key + " q", bits(q), eq)
+        assert_same(key + " dequant", bits(y), oracle.nv_dequantize(eq, esb, np.repeat(es, rows)))
+        del q, sb, s, y
+
+
 def test_config5_layer_step_stream():
     log("config5: generating")
     cfg = workloads.config5()
