@@ -338,6 +338,17 @@ def all_configs(torch, bsq, workloads, dev, reps=21):
     x = a.index_select(0, torch.from_numpy(c5["token_idx"]).to(dev))
     off = torch.from_numpy(c5["offsets"]).to(dev)
     run(5, "routed rows", x, "nv", off)
+    K = x.shape[1]
+    # the same routed rows produced from the 65536 tokens without gathering them: each token
+    # quantized once and written to its 8 routed rows (reads A once instead of X)
+    T = a.shape[0]
+    dst = torch.from_numpy(workloads.scatter_rows(c5["token_idx"], T, 8)).to(dev)
+    s_out = (torch.empty(x.shape[0], K // 2, dtype=torch.uint8, device=dev), torch.empty(x.shape[0], K // 16, dtype=torch.uint8, device=dev),
+             torch.empty(x.shape[0], dtype=torch.float32, device=dev), torch.zeros(1, dtype=torch.int32, device=dev))
+    report(5, "nvfp4 quantize-then-scatter routed rows (from 65536 tokens)", "%dx%d" % tuple(x.shape),
+           2 * T * K + x.shape[0] * (K // 2 + K // 16 + 4) + 8 * dst.numel(), x.numel(),
+           lambda: bsq.nv_quantize_nvfp4_per_token_scatter(a, dst, x.shape[0], *s_out, stream=stream))
+    del s_out
     # the same routed rows as the MoE weight-gradient operand: MXFP8 with 32x1 blocks
     # confined to each expert's rows (partial last blocks), rowwise copy fused or not
     M, K = x.shape

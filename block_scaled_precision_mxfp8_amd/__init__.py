@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.nv_quantize_nvfp4_per_token_grouped.argtypes = [P, I64, I64, P, I64, P, P, P, P, P]
         L.mx_quantize_mxfp8_grouped.restype = I32
         L.mx_quantize_mxfp8_grouped.argtypes = [P, I64, I64, I32, P, I64, P, P, P, P, I64, P, P]
+        L.nv_quantize_nvfp4_per_token_scatter.restype = I32
+        L.nv_quantize_nvfp4_per_token_scatter.argtypes = [P, I64, I64, P, I64, I64, P, P, P, P, P]
         L.nv_quantize_nvfp4_per_group.restype = I32
         L.nv_quantize_nvfp4_per_group.argtypes = [P, I64, I64, P, I64, P, P, P, P, P]
         L.nv_dequantize_per_group.restype = I32
@@ -326,3 +328,28 @@ def nv_dequantize_per_group(q: torch.Tensor, sb: torch.Tensor, s_group: torch.Te
            lib().nv_dequantize_per_group(_ptr(q), _ptr(sb), _ptr(s_group), _ptr(group_offsets), G, R, K,
                                          _ptr(y), _stream(stream)))
     return y
+
+
+def nv_quantize_nvfp4_per_token_scatter(h: torch.Tensor, dst_rows: torch.Tensor, n_rows: int, q=None,
+                                        sb=None, st=None, status=None, stream=None):
+    """Per-token NVFP4 of the routed rows X[dst_rows[t, j]] = h[t] without gathering X:
+    each token of h [T, K] bf16 is quantized once and written to its routed rows
+    (dst_rows int64 [T, top_k] on the GPU; negative = dropped).  Returns (q [N, K/2],
+    sb [N, K/16], st [N], status) for N = n_rows routed rows."""
+    if h.dim() != 2 or dst_rows.dim() != 2:
+        raise ValueError("h and dst_rows must be 2-D")
+    T, K = h.shape
+    _dev_tensor(h, "h", torch.bfloat16, (T, K))
+    top_k = dst_rows.shape[1]
+    _dev_tensor(dst_rows, "dst_rows", torch.int64, (T, top_k))
+    if K % 16:
+        raise ValueError("NVFP4 needs K % 16 == 0")
+    N = int(n_rows)
+    q = _out(q, "q", torch.uint8, (N, K // 2), h)
+    sb = _out(sb, "sb", torch.uint8, (N, K // 16), h)
+    st = _out(st, "st", torch.float32, (N,), h)
+    status = _out(status, "status", torch.int32, (1,), h)
+    _check("nv_quantize_nvfp4_per_token_scatter",
+           lib().nv_quantize_nvfp4_per_token_scatter(_ptr(h), T, K, _ptr(dst_rows), top_k, N, _ptr(q), _ptr(sb),
+                                                     _ptr(st), _ptr(status), _stream(stream)))
+    return q, sb, st, status

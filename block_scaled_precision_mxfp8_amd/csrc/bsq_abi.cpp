@@ -26,6 +26,9 @@ hipError_t launch_nv_quant_group(const void* x, int64_t R, int64_t K, const int6
                                  void* q, void* sb, float* s_group, int32_t* status, hipStream_t stream);
 hipError_t launch_nv_dequant_group(const void* q, const void* sb, const float* s_group, const int64_t* off,
                                    int64_t G, int64_t R, int64_t K, void* y, hipStream_t stream);
+hipError_t launch_nv_quant_scatter(const void* h, int64_t T, int64_t K, const int64_t* dst, int64_t top_k,
+                                   int64_t N, void* q, void* sb, float* st, int32_t* status,
+                                   hipStream_t stream);
 }  // namespace bsq
 
 namespace {
@@ -172,6 +175,33 @@ int nv_quantize_nvfp4_per_token_grouped(const void* x, int64_t R, int64_t K,
                                         void* sb, float* st, int32_t* status_dev,
                                         void* stream) {
     return nv_quant_common(x, R, K, expert_offsets, E, true, q, sb, st, status_dev, stream);
+}
+
+int nv_quantize_nvfp4_per_token_scatter(const void* h, int64_t T, int64_t K, const int64_t* dst_rows,
+                                        int64_t top_k, int64_t N, void* q, void* sb, float* st,
+                                        int32_t* status_dev, void* stream) {
+    if (!size_ok(T, K, 2) || !size_ok(N, K, 2)) return BSQ_ERR_SHAPE;
+    if (K % 16 != 0) return BSQ_ERR_SHAPE;
+    if (top_k < 1 || !size_ok(T, top_k, 8)) return BSQ_ERR_SHAPE;
+    if (status_dev != nullptr && misaligned(status_dev, 4)) return BSQ_ERR_ALIGN;
+    const bool no_rows = (T == 0 || K == 0);
+    if (no_rows && status_dev == nullptr) return BSQ_OK;
+    if (!no_rows) {
+        if (h == nullptr || dst_rows == nullptr) return BSQ_ERR_NULL;
+        if (misaligned(h, 16) || misaligned(dst_rows, 8)) return BSQ_ERR_ALIGN;
+    }
+    const bool out = !no_rows && N > 0;
+    if (out) {
+        if (q == nullptr || sb == nullptr || st == nullptr) return BSQ_ERR_NULL;
+        if (misaligned(q, 16) || misaligned(sb, 16) || misaligned(st, 16)) return BSQ_ERR_ALIGN;
+    }
+    const int64_t nh = no_rows ? 0 : T * K, nx = out ? N * K : 0;
+    const Buf bufs[6] = {{h, 2 * nh}, {dst_rows, no_rows ? 0 : 8 * T * top_k},
+                         {q, nx / 2}, {sb, nx / 16}, {st, out ? 4 * N : 0},
+                         {status_dev, status_dev != nullptr ? 4 : 0}};
+    if (overlap(bufs, 6)) return BSQ_ERR_ALIAS;
+    return hip_status(bsq::launch_nv_quant_scatter(h, no_rows ? 0 : T, K, dst_rows, top_k, N, q, sb, st,
+                                                   status_dev, static_cast<hipStream_t>(stream)));
 }
 
 int nv_quantize_nvfp4_per_group(const void* x, int64_t R, int64_t K, const int64_t* group_offsets,

@@ -157,22 +157,17 @@ __device__ __forceinline__ float nv_decode_scale(uint32_t amax_bf16) {
     return __uint_as_float(amax_bf16 << 16) / 2688.0f;
 }
 
-// Quantize the span held in v (all lanes of the wave take part) under the FP32 decode
-// scales s_a (row r0) and s_b (row r0+1, RPW = 2): n_ch valid chunks.  The span's
-// block-scale bytes are gathered in the wave's LDS slice `lsb` (32 NS bytes) and leave
-// as 16-byte stores when the run is 16-byte aligned.
-template <int NS, int RPW, bool FULL>
-__device__ __forceinline__ void quant_span(const uint4 (&v)[NS], int64_t r0, int n_ch, int cpr,
-                                           float s_a, float s_b,
-                                           uint32_t* __restrict__ q, uint8_t* __restrict__ sb,
-                                           uint8_t* lsb) {
+// Encode the span held in v (all lanes of the wave take part) under the FP32 decode
+// scales s_a (row r0) and s_b (row r0+1, RPW = 2): packed[j] gets the 8 E2M1 codes of the
+// lane's chunk in slot j, and the span's block-scale bytes are gathered in the wave's LDS
+// slice `lsb` (32 NS bytes, byte i = block i of the span), ready when this returns.
+template <int NS, int RPW>
+__device__ __forceinline__ void encode_span(const uint4 (&v)[NS], int cpr, float s_a, float s_b,
+                                            uint32_t (&packed)[NS], uint8_t* lsb) {
     const int lane = threadIdx.x & 63;
     // second row of the span for slot j? (RPW == 2 only; cpr is the row length in chunks)
     auto in_b = [&](int j) { return RPW == 2 && 64 * j + lane >= cpr; };
     const float p_a = 6.0f * s_a, p_b = 6.0f * s_b;                   // fl(6 s)
-
-    uint32_t* qs = q + r0 * cpr;                      // 4 bytes of q per chunk
-    uint8_t* sbs = sb + r0 * (cpr >> 1);              // one scale byte per chunk pair
     const bool odd = (lane & 1) != 0;
     // Slots are taken two at a time: the two lanes of a block pair hold both blocks'
     // maxima, the even lane works out slot j's scale and multiplier, the odd lane slot
@@ -197,21 +192,36 @@ __device__ __forceinline__ void quant_span(const uint4 (&v)[NS], int64_t r0, int
             code1 = odd ? code : oc;
             f1 = odd ? f : of;
         }
-        const int ch0 = 64 * j + lane;
-        const uint32_t packed0 = nv_enc8(v[j], f0);
-        if (FULL || ch0 < n_ch) st_stream<NVQ_NT_STORE>(qs + ch0, packed0);
+        packed[j] = nv_enc8(v[j], f0);
         if (!odd) lsb[32 * j + (lane >> 1)] = (uint8_t)code0;
         if (two) {
-            const int ch1 = 64 * (j + 1) + lane;
-            const uint32_t packed1 = nv_enc8(v[j + 1], f1);
-            if (FULL || ch1 < n_ch) st_stream<NVQ_NT_STORE>(qs + ch1, packed1);
+            packed[j + 1] = nv_enc8(v[j + 1], f1);
             if (!odd) lsb[32 * (j + 1) + (lane >> 1)] = (uint8_t)code1;
         }
     }
-    // the wave's LDS slice: written above by even lanes, read below by the first lanes
+    // the wave's LDS slice: written above by even lanes, read after this by any lane
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Quantize the span held in v into rows r0 .. of q and sb (n_ch valid chunks); the scale
+// bytes leave as 16-byte stores when the span's run is 16-byte aligned.
+template <int NS, int RPW, bool FULL>
+__device__ __forceinline__ void quant_span(const uint4 (&v)[NS], int64_t r0, int n_ch, int cpr,
+                                           float s_a, float s_b,
+                                           uint32_t* __restrict__ q, uint8_t* __restrict__ sb,
+                                           uint8_t* lsb) {
+    const int lane = threadIdx.x & 63;
+    uint32_t packed[NS];
+    encode_span<NS, RPW>(v, cpr, s_a, s_b, packed, lsb);
+    uint32_t* qs = q + r0 * cpr;                      // 4 bytes of q per chunk
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const int ch = 64 * j + lane;
+        if (FULL || ch < n_ch) st_stream<NVQ_NT_STORE>(qs + ch, packed[j]);
+    }
+    uint8_t* sbs = sb + r0 * (cpr >> 1);              // one scale byte per chunk pair
     const int nsb = n_ch >> 1;                        // scale bytes of the span
     if ((nsb & 15) == 0 && ((r0 * (cpr >> 1)) & 15) == 0) {
         if (lane < (nsb >> 4))
@@ -245,6 +255,117 @@ void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
     quant_span<NS, RPW, FULL>(v, r0, n_ch, cpr, s_a, s_b, q, sb, lds_sb[wave]);
     if (lane == 0) st[r0] = s_a;
     if (RPW == 2 && lane == 1 && n_ch > cpr) st[r0 + 1] = s_b;
+}
+
+// ----------------------------------------------------------------------------- scatter
+
+// Quantize-then-scatter of routed rows.  Page "Towards Blackwell-native 8-bit and 4-bit
+// RL", section "Per-token activation scaling": a token's bytes depend on that token only.
+// So the routed rows X[i] = H[t] (a token appears once per expert it is routed to) need
+// not be gathered in BF16 and quantized one by one: each token row of H is quantized once
+// and its bytes are written to every routed row it lands in, bit-identical to quantizing
+// X, while reading H once instead of X (top_k times the bytes).  dst[t][j] is the routed
+// row of token t's j-th choice; a negative entry is a dropped choice, an entry >= N is
+// reported in *status and skipped.
+
+__global__ __launch_bounds__(64)
+void nv_status_clear_kernel(int32_t* __restrict__ status) {
+    if (threadIdx.x == 0) *status = 0;
+}
+
+template <int NS, int RPW, bool FULL>
+__global__ __launch_bounds__(64 * NV_WAVES)
+void nv_quant_scatter_kernel(const uint4* __restrict__ h, int64_t T, int64_t K,
+                             const int64_t* __restrict__ dst, int64_t top_k, int64_t N,
+                             uint32_t* __restrict__ q, uint8_t* __restrict__ sb, float* __restrict__ st,
+                             int32_t* __restrict__ status) {
+    const int wave = wave_id();
+    const int lane = threadIdx.x & 63;
+    const int64_t r0 = ((int64_t)blockIdx.x * NV_WAVES + wave) * RPW;
+    if (r0 >= T) return;
+    __shared__ __align__(16) uint8_t lds_sb[NV_WAVES][32 * NS];
+    const int cpr = (int)(K >> 3);
+    const int n_ch = (RPW == 2 && r0 + 1 >= T) ? cpr : RPW * cpr;
+    const bool has_b = RPW == 2 && n_ch > cpr;
+    uint4 v[NS];
+    load_span<NS, FULL>(v, h + r0 * cpr, n_ch);
+    const uint32_t mm = span_amax<NS, RPW>(v, cpr);
+    const float s_a = nv_decode_scale(mm & 0xFFFFu);
+    const float s_b = nv_decode_scale(mm >> 16);
+    uint32_t packed[NS];
+    uint8_t* lsb = lds_sb[wave];
+    encode_span<NS, RPW>(v, cpr, s_a, s_b, packed, lsb);
+    const int sbr = cpr >> 1;                         // scale bytes per row
+    const bool sb16 = (sbr & 15) == 0;                // a row's scale run is whole 16-byte units
+    for (int64_t c = 0; c < top_k; ++c) {
+        const int64_t da = dst[r0 * top_k + c];
+        const int64_t db = has_b ? dst[(r0 + 1) * top_k + c] : -1;
+        const bool va = da >= 0 && da < N, vb = db >= 0 && db < N;
+        if (status != nullptr && lane == 0 && (da >= N || db >= N)) *status = 6;   // BSQ_ERR_OFFSETS
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const int ch = 64 * j + lane;
+            const bool inb = RPW == 2 && ch >= cpr;
+            if ((FULL || ch < n_ch) && (inb ? vb : va))
+                st_stream<NVQ_NT_STORE>(q + (inb ? db : da) * cpr + (inb ? ch - cpr : ch), packed[j]);
+        }
+        if (sb16) {
+            const int units = sbr >> 4;               // 16-byte units per row
+            const bool inb = lane >= units;
+            if (lane < (has_b ? 2 : 1) * units && (inb ? vb : va))
+                st_stream<NVQ_NT_STORE>(reinterpret_cast<uint4*>(sb + (inb ? db : da) * sbr) + (inb ? lane - units : lane),
+                                        reinterpret_cast<const uint4*>(lsb)[lane]);
+        } else {
+            for (int i = lane; i < (has_b ? 2 : 1) * sbr; i += 64) {
+                const bool inb = i >= sbr;
+                if (inb ? vb : va) sb[(inb ? db : da) * sbr + (inb ? i - sbr : i)] = lsb[i];
+            }
+        }
+        if (lane == 0 && va) st[da] = s_a;
+        if (lane == 1 && vb) st[db] = s_b;
+    }
+}
+
+// Tokens longer than the register-resident variants: one wave per token, the row streamed
+// twice, each chunk's codes written to every destination.
+__global__ __launch_bounds__(64 * NV_WAVES)
+void nv_quant_scatter_long_kernel(const uint4* __restrict__ h, int64_t T, int64_t K,
+                                  const int64_t* __restrict__ dst, int64_t top_k, int64_t N,
+                                  uint32_t* __restrict__ q, uint8_t* __restrict__ sb, float* __restrict__ st,
+                                  int32_t* __restrict__ status) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * NV_WAVES + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int64_t cpr = K >> 3;
+    const uint4* xr = h + t * cpr;
+    uint32_t m = 0u;
+    for (int64_t base = 0; base < cpr; base += 64) {
+        const int64_t ch = base + lane;
+        if (ch < cpr) m = max(m, chunk_absmax8(xr[ch]));
+    }
+    const float s = nv_decode_scale(wave_max(m));
+    const float p = 6.0f * s;
+    for (int64_t c = 0; c < top_k; ++c) {
+        const int64_t d = dst[t * top_k + c];
+        if (status != nullptr && lane == 0 && d >= N) *status = 6;
+        if (lane == 0 && d >= 0 && d < N) st[d] = s;
+    }
+    for (int64_t base = 0; base < cpr; base += 64) {
+        const int64_t ch = base + lane;
+        const uint4 v = (ch < cpr) ? xr[ch] : make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t amax_b = pair_max(chunk_absmax8(v));
+        float f;
+        const uint32_t code = nv_block_scale(amax_b, s, p, f);
+        const uint32_t packed = nv_enc8(v, f);
+        if (ch < cpr) {
+            for (int64_t c = 0; c < top_k; ++c) {
+                const int64_t d = dst[t * top_k + c];
+                if (d < 0 || d >= N) continue;
+                q[d * cpr + ch] = packed;
+                if ((lane & 1) == 0) sb[d * (K >> 4) + (ch >> 1)] = (uint8_t)code;
+            }
+        }
+    }
 }
 
 // ----------------------------------------------------------------------------- per group
@@ -661,6 +782,55 @@ hipError_t launch_nv_quant_group(const void* x, int64_t R, int64_t K, const int6
         }
     }
     hipLaunchKernelGGL(nv_group_finalize_kernel, dim3(gg), dim3(256), 0, stream, s_group, G);
+    return hipGetLastError();
+}
+
+template <int NS, int RPW>
+static void launch_scatter(const void* h, int64_t T, int64_t K, const int64_t* dst, int64_t top_k, int64_t N,
+                           void* q, void* sb, float* st, int32_t* status, hipStream_t stream) {
+    const int64_t spans = (T + RPW - 1) / RPW;
+    const int64_t grid = (spans + NV_WAVES - 1) / NV_WAVES;
+    const bool full = RPW * K == 512 * NS && T % RPW == 0;
+    if (full)
+        hipLaunchKernelGGL((nv_quant_scatter_kernel<NS, RPW, true>), dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
+                           stream, (const uint4*)h, T, K, dst, top_k, N, (uint32_t*)q, (uint8_t*)sb, st, status);
+    else
+        hipLaunchKernelGGL((nv_quant_scatter_kernel<NS, RPW, false>), dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
+                           stream, (const uint4*)h, T, K, dst, top_k, N, (uint32_t*)q, (uint8_t*)sb, st, status);
+}
+
+hipError_t launch_nv_quant_scatter(const void* h, int64_t T, int64_t K, const int64_t* dst, int64_t top_k,
+                                   int64_t N, void* q, void* sb, float* st, int32_t* status,
+                                   hipStream_t stream) {
+    if (status != nullptr)
+        hipLaunchKernelGGL(nv_status_clear_kernel, dim3(1), dim3(64), 0, stream, status);
+    if (T == 0 || K == 0 || N == 0) {
+        if (T > 0 && K > 0 && status != nullptr) {   // no rows to write, but report bad entries
+            hipLaunchKernelGGL(nv_quant_scatter_long_kernel, dim3((unsigned)((T + NV_WAVES - 1) / NV_WAVES)),
+                               dim3(64 * NV_WAVES), 0, stream, (const uint4*)h, T, K, dst, top_k, N,
+                               (uint32_t*)q, (uint8_t*)sb, st, status);
+        }
+        return hipGetLastError();
+    }
+    if (K <= NV_PAIR_MAX_K) {
+        switch ((2 * (K / 8) + 63) / 64) {
+            case 1: launch_scatter<1, 2>(h, T, K, dst, top_k, N, q, sb, st, status, stream); break;
+            case 2: launch_scatter<2, 2>(h, T, K, dst, top_k, N, q, sb, st, status, stream); break;
+            default: launch_scatter<3, 2>(h, T, K, dst, top_k, N, q, sb, st, status, stream); break;
+        }
+        return hipGetLastError();
+    }
+    switch ((K / 8 + 63) / 64) {
+        case 2: launch_scatter<2, 1>(h, T, K, dst, top_k, N, q, sb, st, status, stream); break;
+        case 3: launch_scatter<3, 1>(h, T, K, dst, top_k, N, q, sb, st, status, stream); break;
+        case 4: launch_scatter<4, 1>(h, T, K, dst, top_k, N, q, sb, st, status, stream); break;
+        case 5: case 6: launch_scatter<6, 1>(h, T, K, dst, top_k, N, q, sb, st, status, stream); break;
+        case 7: case 8: launch_scatter<8, 1>(h, T, K, dst, top_k, N, q, sb, st, status, stream); break;
+        default:
+            hipLaunchKernelGGL(nv_quant_scatter_long_kernel, dim3((unsigned)((T + NV_WAVES - 1) / NV_WAVES)),
+                               dim3(64 * NV_WAVES), 0, stream, (const uint4*)h, T, K, dst, top_k, N,
+                               (uint32_t*)q, (uint8_t*)sb, st, status);
+    }
     return hipGetLastError();
 }
 

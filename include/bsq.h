@@ -144,6 +144,25 @@ int mx_quantize_mxfp8_grouped(const void* x_bf16, int64_t M, int64_t K, int mode
                               int32_t* status_dev, void* stream);
 
 /*
+ * Per-token NVFP4 of routed rows without gathering them: quantize-then-scatter.
+ * Passage: "Per-token activation scaling" (a token's bytes depend on that token only).
+ * The routed rows are X[dst[t][j]] = H[t] for every token t < T and choice j < top_k (a
+ * token is routed to top_k experts); this call quantizes each token row of H[T][K] once and
+ * writes its q / sb / st to each of its routed rows, so the outputs are exactly those of
+ * nv_quantize_nvfp4_per_token on X (N rows) while H is read once instead of X.
+ * dst_rows: DEVICE int64 [T][top_k], the routed row of each (token, choice); a negative
+ * entry is a dropped choice; entries must be distinct.  Rows of X that no entry names are
+ * not written.  Needs K % 16 == 0.  Outputs as nv_quantize_nvfp4_per_token on N rows:
+ *   q u8 [N][K/2],  sb u8 [N][K/16],  st f32 [N].
+ * If status_dev is not NULL the kernel writes BSQ_ERR_OFFSETS to *status_dev when an entry
+ * is >= N (it is skipped) and BSQ_OK otherwise.
+ */
+int nv_quantize_nvfp4_per_token_scatter(const void* h_bf16, int64_t T, int64_t K,
+                                        const int64_t* dst_rows, int64_t top_k, int64_t N,
+                                        void* q, void* sb, float* st,
+                                        int32_t* status_dev, void* stream);
+
+/*
  * Standard NVFP4 of x[R][K] (BF16) with one FP32 scale per group of rows: rows
  * [offsets[g], offsets[g+1]) form group g (a whole tensor, or one expert's tensor; an
  * expert's gate and up projections belong in one group).

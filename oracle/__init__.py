@@ -278,6 +278,23 @@ def nv_quantize_per_token_grouped(x: np.ndarray, offsets: np.ndarray):
     return q, sb, st, ok
 
 
+def nv_quantize_per_token_routed(h: np.ndarray, dst: np.ndarray, n_rows: int):
+    """Per-token NVFP4 of the routed rows X[dst[t, j]] = h[t] (negative dst = dropped),
+    computed the plain way: gather X, then quantize every row.  Returns (q, sb, st,
+    written) where written marks the rows some entry names."""
+    h = _as_bf16_bits(h)
+    T, K = h.shape
+    dst = np.asarray(dst, dtype=np.int64).reshape(T, -1)
+    x = np.zeros((n_rows, K), np.uint16)
+    written = np.zeros(n_rows, bool)
+    for j in range(dst.shape[1]):
+        keep = dst[:, j] >= 0
+        x[dst[keep, j]] = h[keep]
+        written[dst[keep, j]] = True
+    q, sb, st = nv_quantize_per_token(x)
+    return q, sb, st, written
+
+
 def nv_quantize_per_group(x: np.ndarray, offsets):
     """Standard NVFP4 with one FP32 scale per row group (a tensor, or an expert's tensor with
     gate and up together): groups are row ranges offsets int64[G+1].  Returns (q[R][K/2],

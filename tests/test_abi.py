@@ -42,7 +42,7 @@ def _declared_functions():
 def test_header_declares_the_expected_entry_points():
     names = _declared_functions()
     for n in ("mx_quantize_mxfp8", "mx_quantize_mxfp8_grouped", "nv_quantize_nvfp4_per_group",
-              "nv_dequantize_per_group", "nv_quantize_nvfp4_per_token",
+              "nv_dequantize_per_group", "nv_quantize_nvfp4_per_token_scatter", "nv_quantize_nvfp4_per_token",
               "nv_quantize_nvfp4_per_token_grouped", "mx_dequantize", "nv_dequantize",
               "bsq_status_string", "bsq_abi_version"):
         assert n in names
@@ -188,6 +188,24 @@ def test_nv_per_group_validation(L):
     assert f(A, B, C, D + 4, 2, 4, 64, E_, None) == bsq.BSQ_ERR_ALIGN
     assert f(A, B, C, D, 2, 4, 64, A + 16, None) == bsq.BSQ_ERR_ALIAS
     assert f(A, B, C, D, 2, 0, 64, E_, None) == bsq.BSQ_OK
+
+
+def test_nv_scatter_validation(L):
+    def f(h=A, T=4, K=64, dst=E_, top_k=2, N=8, q=B, sb=C, st=D, status=None):
+        return L.nv_quantize_nvfp4_per_token_scatter(h, T, K, dst, top_k, N, q, sb, st, status, None)
+    assert f(K=40) == bsq.BSQ_ERR_SHAPE
+    assert f(T=-1) == bsq.BSQ_ERR_SHAPE
+    assert f(N=-1) == bsq.BSQ_ERR_SHAPE
+    assert f(top_k=0) == bsq.BSQ_ERR_SHAPE
+    assert f(h=None) == bsq.BSQ_ERR_NULL
+    assert f(dst=None) == bsq.BSQ_ERR_NULL
+    assert f(st=None) == bsq.BSQ_ERR_NULL
+    assert f(dst=E_ + 4) == bsq.BSQ_ERR_ALIGN
+    assert f(q=B + 8) == bsq.BSQ_ERR_ALIGN
+    assert f(q=A + 16) == bsq.BSQ_ERR_ALIAS                    # output inside the input
+    assert f(dst=C) == bsq.BSQ_ERR_ALIAS                       # map inside sb
+    assert f(T=0) == bsq.BSQ_OK                                # nothing to do, no status asked
+    assert f(N=0, q=None, sb=None, st=None, T=0) == bsq.BSQ_OK
 
 
 # ---------------------------------------------------------------------------------------

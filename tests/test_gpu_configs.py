@@ -196,3 +196,28 @@ def test_config5_routed_rows_mxfp8_grouped_by_expert():
     rows_d = torch.from_numpy(rows).cuda()
     assert_same("X q_row", bits(q_row.index_select(0, rows_d)), er)
     assert_same("X s_row", bits(s_row.index_select(0, rows_d)), esr)
+
+
+def test_config5_routed_rows_by_quantize_then_scatter():
+    """The layer step's 524288 routed rows produced from the 65536 tokens directly: each
+    token quantized once and written to its 8 routed rows.  Compared with the CPU oracle
+    (gather, then quantize) on a seeded sample of rows, and with the direct path (gather in
+    BF16, grouped quantize) on every byte."""
+    log("config5 scatter: generating")
+    cfg = workloads.config5()
+    a, tok, off = cfg["a"], cfg["token_idx"], cfg["offsets"]
+    dst = workloads.scatter_rows(tok, a.shape[0], 8)
+    ad = to_dev(a)
+    q, sb, st, status = bsq.nv_quantize_nvfp4_per_token_scatter(ad, torch.from_numpy(dst).cuda(), tok.size)
+    xq, xsb, xst, xstatus = bsq.nv_quantize_nvfp4_per_token_grouped(
+        ad.index_select(0, torch.from_numpy(tok).cuda()), torch.from_numpy(off).cuda())
+    torch.cuda.synchronize()
+    assert int(status.item()) == bsq.BSQ_OK and int(xstatus.item()) == bsq.BSQ_OK
+    assert torch.equal(q, xq) and torch.equal(sb, xsb) and torch.equal(st.view(torch.int32), xst.view(torch.int32))
+    log("config5 scatter: comparing sampled rows")
+    rows = np.sort(np.random.default_rng(58).choice(tok.size, 8192, replace=False))
+    eq, esb, est = oracle.nv_quantize_per_token(a[tok[rows]])
+    rows_d = torch.from_numpy(rows).cuda()
+    assert_same("scatter q", bits(q.index_select(0, rows_d)), eq)
+    assert_same("scatter sb", bits(sb.index_select(0, rows_d)), esb)
+    assert_same("scatter st", bits(st.index_select(0, rows_d)), est.view(np.uint32))

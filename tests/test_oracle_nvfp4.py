@@ -344,3 +344,24 @@ def test_per_group_rejects_bad_offsets():
     x = np.zeros((8, 16), np.uint16)
     for off in ([1, 8], [0, 5, 3, 8], [0, 7]):
         assert oracle.nv_quantize_per_group(x, off)[3] is False
+
+
+# --------------------------------------------------------------------------- routed rows
+
+def test_quantize_then_gather_equals_gather_then_quantize():
+    """Per-token scaling is row-local ("Per-token activation scaling": no token's bytes
+    depend on other tokens), so quantizing the tokens once and gathering the packed rows
+    gives the bytes of quantizing the gathered BF16 rows."""
+    rng = np.random.default_rng(31)
+    T, K, k = 40, 96, 3
+    h = _rand_rows(rng, T, K)
+    tok = np.concatenate([rng.permutation(T) for _ in range(k)])     # each token k times
+    dst = workloads.scatter_rows(tok, T, k)
+    assert np.all(tok[dst] == np.arange(T)[:, None])
+    q, sb, st, written = oracle.nv_quantize_per_token_routed(h, dst, T * k)
+    assert written.all()
+    hq, hsb, hst = oracle.nv_quantize_per_token(h)
+    assert np.array_equal(q, hq[tok]) and np.array_equal(sb, hsb[tok])
+    assert np.array_equal(st.view(np.uint32), hst[tok].view(np.uint32))
+    gq, gsb, gst = oracle.nv_quantize_per_token(h[tok])
+    assert np.array_equal(q, gq) and np.array_equal(sb, gsb)

@@ -162,3 +162,13 @@ def config5(seed: int = 4, tokens: int = 65536, hidden: int = HIDDEN, w_cols: in
     if materialize:
         out["x"] = a[token_idx]
     return out
+
+
+def scatter_rows(token_idx: np.ndarray, tokens: int, top_k: int) -> np.ndarray:
+    """Inverse of a routed-row gather: dst[t, j] = the routed row holding token t's j-th
+    occurrence in token_idx (each token appears exactly top_k times)."""
+    tok = np.asarray(token_idx, dtype=np.int64)
+    assert tok.size == tokens * top_k
+    order = np.argsort(tok, kind="stable")                   # routed rows grouped by token
+    assert np.array_equal(tok[order], np.repeat(np.arange(tokens), top_k))
+    return order.reshape(tokens, top_k).astype(np.int64)
