@@ -87,6 +87,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_nv_quantize_per_token.argtypes = [P, I64, I64, P, P, P]
         L.oracle_nv_quantize_per_group.restype = None
         L.oracle_nv_quantize_per_group.argtypes = [P, I64, I64, P, I64, P, P, P]
+        L.oracle_nv_quantize_2d.restype = None
+        L.oracle_nv_quantize_2d.argtypes = [P, I64, I64, P, I64, P, P, P]
+        L.oracle_nv_dequantize_2d.restype = None
+        L.oracle_nv_dequantize_2d.argtypes = [P, P, P, P, I64, I64, I64, P]
         L.oracle_nv_dequantize.restype = None
         L.oracle_nv_dequantize.argtypes = [P, P, P, I64, I64, P]
         for name in ("oracle_enc_e4m3_array", "oracle_enc_e2m1_array", "oracle_rne_bf16_array"):
@@ -314,6 +318,40 @@ def nv_quantize_per_group(x: np.ndarray, offsets):
     s = np.empty(G, np.float32)
     lib().oracle_nv_quantize_per_group(_ptr(x), R, K, _ptr(off), G, _ptr(q), _ptr(sb), _ptr(s))
     return q, sb, s, True
+
+
+def nv_quantize_2d(x: np.ndarray, offsets):
+    """NVFP4 with 16x16 weight tiles (one E4M3 scale per tile) under one FP32 scale per row
+    group.  x[R][K] with R % 16 == K % 16 == 0, every group whole tiles.  Returns
+    (q[R][K/2], sb[R/16][K/16], s_group[G] float32, ok); ok False (arrays None) for
+    invalid offsets or shapes."""
+    x = _as_bf16_bits(x)
+    R, K = x.shape
+    off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    ok = bool(R % 16 == 0 and K % 16 == 0 and off.ndim == 1 and off.size >= 2 and off[0] == 0
+              and off[-1] == R and np.all(np.diff(off) >= 0) and np.all(off % 16 == 0))
+    if not ok:
+        return None, None, None, False
+    G = off.size - 1
+    q = np.empty((R, K // 2), np.uint8)
+    sb = np.empty((R // 16, K // 16), np.uint8)
+    s = np.empty(G, np.float32)
+    lib().oracle_nv_quantize_2d(_ptr(x), R, K, _ptr(off), G, _ptr(q), _ptr(sb), _ptr(s))
+    return q, sb, s, True
+
+
+def nv_dequantize_2d(q: np.ndarray, sb: np.ndarray, s_group: np.ndarray, offsets) -> np.ndarray:
+    """BF16 bits of the 16x16-tile NVFP4 layout (see nv_quantize_2d)."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    sb = np.ascontiguousarray(sb, dtype=np.uint8)
+    s = np.ascontiguousarray(s_group, dtype=np.float32)
+    off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    R, half = q.shape
+    K = 2 * half
+    assert sb.shape == (R // 16, K // 16) and s.shape == (off.size - 1,)
+    y = np.empty((R, K), np.uint16)
+    lib().oracle_nv_dequantize_2d(_ptr(q), _ptr(sb), _ptr(s), _ptr(off), off.size - 1, R, K, _ptr(y))
+    return y
 
 
 def nv_dequantize(q: np.ndarray, sb: np.ndarray, st: np.ndarray) -> np.ndarray:

@@ -393,6 +393,79 @@ void oracle_nv_quantize_per_group(const uint16_t* x, int64_t R, int64_t K,
     }
 }
 
+/* NVFP4 with 16x16 weight blocks (two-dimensional block scaling of the weights, one of the
+ * four parts of NVIDIA's NVFP4 pretraining recipe: page "NVIDIA verified the 4-bit NVFP4
+ * format on a Mamba-Transformer (12B) at 10 trillion tokens"; Miles turns it off, "Towards
+ * Blackwell-native 8-bit and 4-bit RL", section "Try the NVFP4 recipe in Miles"): every 16x16 tile of a
+ * weight shares one E4M3 scale, under the FP32 scale of its row group (as in
+ * oracle_nv_quantize_per_group), so the same codes and scales serve the weight and its
+ * transpose.  Reading: the per-token steps with the tile in place of the 1x16 block:
+ *   s_g = fl(amax_g / 2688);  sb = ENC_E4M3(fl(amax_tile / fl(6 s_g)));
+ *   f = min(fl(1 / fl(DEC(sb) s_g)), FLT_MAX) (0 if that product is 0);  q = ENC_E2M1(fl(x f)).
+ * x[R][K], R % 16 == 0, K % 16 == 0, every group a whole number of 16-row tiles (the
+ * caller checks).  q[R][K/2] packed as usual, sb[R/16][K/16], s_group[G]. */
+void oracle_nv_quantize_2d(const uint16_t* x, int64_t R, int64_t K, const int64_t* off, int64_t G,
+                           uint8_t* q, uint8_t* sb, float* s_group) {
+    build_tables();
+    (void)R;
+    for (int64_t g = 0; g < G; ++g) {
+        double amax = 0.0;
+        for (int64_t r = off[g]; r < off[g + 1]; ++r) {
+            double a = bf16_amax(x + r * K, K);
+            if (a > amax) amax = a;
+        }
+        s_group[g] = oracle_nv_token_scale((float)amax);
+    }
+    const int64_t tiles_r = off[G] / 16, tiles_c = K / 16;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t tr = 0; tr < tiles_r; ++tr) {
+        int64_t g = 0;
+        while (off[g + 1] <= tr * 16) ++g;                /* the group of the tile's rows */
+        const float s = s_group[g];
+        for (int64_t tc = 0; tc < tiles_c; ++tc) {
+            double amax_t = 0.0;
+            for (int i = 0; i < 16; ++i) {
+                double a = bf16_amax(x + (tr * 16 + i) * K + tc * 16, 16);
+                if (a > amax_t) amax_t = a;
+            }
+            uint8_t code = oracle_nv_block_scale((float)amax_t, s);
+            sb[tr * tiles_c + tc] = code;
+            float f = oracle_nv_block_multiplier(code, s);
+            for (int i = 0; i < 16; ++i) {
+                const uint16_t* xr = x + (tr * 16 + i) * K + tc * 16;
+                for (int j = 0; j < 16; j += 2) {
+                    float x0 = (float)oracle_bf16_to_double(xr[j]);
+                    float x1 = (float)oracle_bf16_to_double(xr[j + 1]);
+                    uint8_t c0 = oracle_enc_e2m1((double)(x0 * f));
+                    uint8_t c1 = oracle_enc_e2m1((double)(x1 * f));
+                    q[(tr * 16 + i) * (K / 2) + (tc * 16 + j) / 2] = (uint8_t)(c0 | (c1 << 4));
+                }
+            }
+        }
+    }
+}
+
+/* Dequantization of the 16x16-tile layout: y = RNE_BF16(fl(exact(DEC_E2M1(q) *
+ * DEC_E4M3(sb[r/16][c/16])) * s_g)) with s_g the scale of row r's group. */
+void oracle_nv_dequantize_2d(const uint8_t* q, const uint8_t* sb, const float* s_group,
+                             const int64_t* off, int64_t G, int64_t R, int64_t K, uint16_t* y) {
+    build_tables();
+    (void)G;
+    const int64_t tiles_c = K / 16;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        int64_t g = 0;
+        while (off[g + 1] <= r) ++g;
+        for (int64_t k = 0; k < K; ++k) {
+            uint8_t byte = q[r * (K / 2) + k / 2];
+            uint8_t code = (k & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 0xF);
+            uint8_t bs = sb[(r / 16) * tiles_c + k / 16];
+            double e = oracle_dec_e2m1(code) * oracle_dec_e4m3(bs);   /* exact */
+            y[r * K + k] = oracle_rne_bf16((double)((float)e * s_group[g]));
+        }
+    }
+}
+
 /* NVFP4 dequantization: y = RNE_BF16(fl(exact(DEC_E2M1(q) * DEC_E4M3(sb)) * s_t)). */
 void oracle_nv_dequantize(const uint8_t* q, const uint8_t* sb, const float* st,
                           int64_t R, int64_t K, uint16_t* y) {

@@ -365,3 +365,65 @@ def test_quantize_then_gather_equals_gather_then_quantize():
     assert np.array_equal(st.view(np.uint32), hst[tok].view(np.uint32))
     gq, gsb, gst = oracle.nv_quantize_per_token(h[tok])
     assert np.array_equal(q, gq) and np.array_equal(sb, gsb)
+
+
+# --------------------------------------------------------------------------- 16x16 tiles
+
+def _unpack(q):
+    lo, hi = q & 0xF, q >> 4
+    return np.stack([lo, hi], axis=-1).reshape(q.shape[0], -1)
+
+
+def test_2d_golden():
+    g = _golden("nvfp4_2d_tile.txt")
+    x = np.full((16, 16), g["x_other"][0], np.uint16)
+    x[0, 0] = g["x00"][0]
+    q, sb, s, ok = oracle.nv_quantize_2d(x, [0, 16])
+    assert ok and sb.shape == (1, 1)
+    assert s.view(np.uint32)[0] == g["group_scale_f32"][0] and sb[0, 0] == g["tile_sb"][0]
+    assert q[0, 0] == g["q_byte0_row0"][0]
+    rest = np.ones(q.shape, bool)
+    rest[0, 0] = False
+    assert np.all(q[rest] == g["q_other"][0])
+    y = oracle.nv_dequantize_2d(q, sb, s, [0, 16])
+    assert y[0, 0] == g["dequant00"][0]
+    ym = np.ones(y.shape, bool)
+    ym[0, 0] = False
+    assert np.all(y[ym] == g["dequant_other"][0])
+    q1, sb1, s1, _ = oracle.nv_quantize_per_group(x, [0, 16])
+    assert np.all(sb1[1:, 0] == g["rowblock_sb_rows1to15"][0])
+    assert np.all(oracle.nv_dequantize(q1, sb1, np.repeat(s1, 16))[1:] == g["rowblock_dequant_rows1to15"][0])
+
+
+def test_2d_transpose_gives_transposed_codes_and_scales():
+    """Square blocks: the weight and its transpose share codes and scales (the point of
+    two-dimensional blocks is that one quantized copy serves both GEMM orientations)."""
+    rng = np.random.default_rng(41)
+    w = _rand_rows(rng, 48, 80)
+    q, sb, s, ok = oracle.nv_quantize_2d(w, [0, 48])
+    qt, sbt, st_, okt = oracle.nv_quantize_2d(np.ascontiguousarray(w.T), [0, 80])
+    assert ok and okt
+    assert np.array_equal(_unpack(q).T, _unpack(qt))
+    assert np.array_equal(sb.T, sbt)
+    assert s.view(np.uint32)[0] == st_.view(np.uint32)[0]
+
+
+def test_2d_with_identical_rows_in_each_tile_equals_1x16_blocks():
+    """When the 16 rows of every tile are equal, each 1x16 block has the tile's maximum,
+    so the tile scale and codes are those of the per-group 1x16 layout."""
+    rng = np.random.default_rng(42)
+    base = _rand_rows(rng, 5, 64)
+    w = np.repeat(base, 16, axis=0)                            # 80 rows, tiles of equal rows
+    off = [0, 32, 32, 80]
+    q, sb, s, ok = oracle.nv_quantize_2d(w, off)
+    q1, sb1, s1, ok1 = oracle.nv_quantize_per_group(w, off)
+    assert ok and ok1
+    assert np.array_equal(q, q1)
+    assert np.array_equal(np.repeat(sb, 16, axis=0), sb1)
+    assert np.array_equal(s.view(np.uint32), s1.view(np.uint32))
+
+
+def test_2d_rejects_partial_tiles():
+    x = np.zeros((32, 32), np.uint16)
+    assert oracle.nv_quantize_2d(x, [0, 8, 32])[3] is False              # group not whole tiles
+    assert oracle.nv_quantize_2d(np.zeros((24, 32), np.uint16), [0, 24])[3] is False
