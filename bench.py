@@ -328,8 +328,16 @@ def all_configs(torch, bsq, workloads, dev, reps=21):
         report(4, "nvfp4 per-expert-scale dequant " + key, "%dx%d" % (M, K),
                2 * M * K + M * K // 2 + M * K // 16 + 4 * G, M * K,
                lambda: bsq.nv_dequantize_per_group(g_out[0], g_out[1], g_out[2], off, y, stream=stream))
+        # the same export with 16x16 tiles (two-dimensional block scaling)
+        t_out = (g_out[0], torch.empty(M // 16, K // 16, dtype=torch.uint8, device=dev), g_out[2], g_out[3])
+        report(4, "nvfp4 16x16-tile quant (two passes) " + key, "%dx%d" % (M, K),
+               4 * M * K + M * K // 2 + M * K // 256 + 4 * G, M * K,
+               lambda: bsq.nv_quantize_nvfp4_2d(w, off, *t_out, stream=stream))
+        report(4, "nvfp4 16x16-tile dequant " + key, "%dx%d" % (M, K),
+               2 * M * K + M * K // 2 + M * K // 256 + 4 * G, M * K,
+               lambda: bsq.nv_dequantize_2d(t_out[0], t_out[1], t_out[2], off, y, stream=stream))
         torch.cuda.synchronize()
-        del w, g_out, y
+        del w, g_out, t_out, y
     del c4
     c5 = workloads.config5()
     a, w = bf(c5["a"]), bf(c5["w"])

@@ -13,6 +13,7 @@ Layouts (all row-major, all on the GPU):
   MXFP8 grouped     q_col u8 [K, M]      s_col u8 [K, s_ld]   (32x1 blocks per expert)
   NVFP4 per token   q u8 [R, K/2]        sb u8 [R, K/16]      st f32 [R]
   NVFP4 per group   q u8 [R, K/2]        sb u8 [R, K/16]      s_group f32 [G]
+  NVFP4 16x16 tiles q u8 [R, K/2]        sb u8 [R/16, K/16]   s_group f32 [G]
 BF16 tensors are ``torch.bfloat16``.
 """
 from __future__ import annotations
@@ -72,6 +73,10 @@ def lib() -> ctypes.CDLL:
         L.mx_quantize_mxfp8_grouped.argtypes = [P, I64, I64, I32, P, I64, P, P, P, P, I64, P, P]
         L.nv_quantize_nvfp4_per_token_scatter.restype = I32
         L.nv_quantize_nvfp4_per_token_scatter.argtypes = [P, I64, I64, P, I64, I64, P, P, P, P, P]
+        L.nv_quantize_nvfp4_2d.restype = I32
+        L.nv_quantize_nvfp4_2d.argtypes = [P, I64, I64, P, I64, P, P, P, P, P]
+        L.nv_dequantize_2d.restype = I32
+        L.nv_dequantize_2d.argtypes = [P, P, P, P, I64, I64, I64, P, P]
         L.nv_quantize_nvfp4_per_group.restype = I32
         L.nv_quantize_nvfp4_per_group.argtypes = [P, I64, I64, P, I64, P, P, P, P, P]
         L.nv_dequantize_per_group.restype = I32
@@ -353,3 +358,49 @@ def nv_quantize_nvfp4_per_token_scatter(h: torch.Tensor, dst_rows: torch.Tensor,
            lib().nv_quantize_nvfp4_per_token_scatter(_ptr(h), T, K, _ptr(dst_rows), top_k, N, _ptr(q), _ptr(sb),
                                                      _ptr(st), _ptr(status), _stream(stream)))
     return q, sb, st, status
+
+
+def nv_quantize_nvfp4_2d(x: torch.Tensor, group_offsets: torch.Tensor, q=None, sb=None, s_group=None,
+                         status=None, stream=None):
+    """NVFP4 of a weight x [R, K] bf16 with one E4M3 scale per 16x16 tile under one FP32
+    scale per row group (group_offsets int64 [G+1] on the GPU, multiples of 16).  Returns
+    (q [R, K/2], sb [R/16, K/16], s_group [G] f32, status)."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    R, K = x.shape
+    _dev_tensor(x, "x", torch.bfloat16, (R, K))
+    if group_offsets.dim() != 1 or group_offsets.numel() < 2:
+        raise ValueError("group_offsets must be int64 [G+1] with G >= 1")
+    G = group_offsets.numel() - 1
+    _dev_tensor(group_offsets, "group_offsets", torch.int64, (G + 1,))
+    if R % 16 or K % 16:
+        raise ValueError("16x16 tiles need R % 16 == 0 and K % 16 == 0")
+    q = _out(q, "q", torch.uint8, (R, K // 2), x)
+    sb = _out(sb, "sb", torch.uint8, (R // 16, K // 16), x)
+    s_group = _out(s_group, "s_group", torch.float32, (G,), x)
+    status = _out(status, "status", torch.int32, (1,), x)
+    _check("nv_quantize_nvfp4_2d",
+           lib().nv_quantize_nvfp4_2d(_ptr(x), R, K, _ptr(group_offsets), G, _ptr(q), _ptr(sb), _ptr(s_group),
+                                      _ptr(status), _stream(stream)))
+    return q, sb, s_group, status
+
+
+def nv_dequantize_2d(q: torch.Tensor, sb: torch.Tensor, s_group: torch.Tensor, group_offsets: torch.Tensor,
+                     y=None, stream=None) -> torch.Tensor:
+    """BF16 [R, K] from the 16x16-tile NVFP4 layout."""
+    if q.dim() != 2:
+        raise ValueError("q must be 2-D")
+    R, half = q.shape
+    K = 2 * half
+    _dev_tensor(q, "q", torch.uint8, (R, half))
+    if R % 16 or K % 16:
+        raise ValueError("16x16 tiles need R % 16 == 0 and K % 16 == 0")
+    G = group_offsets.numel() - 1
+    _dev_tensor(group_offsets, "group_offsets", torch.int64, (G + 1,))
+    _dev_tensor(sb, "sb", torch.uint8, (R // 16, K // 16))
+    _dev_tensor(s_group, "s_group", torch.float32, (G,))
+    y = _out(y, "y", torch.bfloat16, (R, K), q)
+    _check("nv_dequantize_2d",
+           lib().nv_dequantize_2d(_ptr(q), _ptr(sb), _ptr(s_group), _ptr(group_offsets), G, R, K, _ptr(y),
+                                  _stream(stream)))
+    return y

@@ -29,6 +29,10 @@ hipError_t launch_nv_dequant_group(const void* q, const void* sb, const float* s
 hipError_t launch_nv_quant_scatter(const void* h, int64_t T, int64_t K, const int64_t* dst, int64_t top_k,
                                    int64_t N, void* q, void* sb, float* st, int32_t* status,
                                    hipStream_t stream);
+hipError_t launch_nv_quant_2d(const void* x, int64_t R, int64_t K, const int64_t* off, int64_t G,
+                              void* q, void* sb, float* s_group, int32_t* status, hipStream_t stream);
+hipError_t launch_nv_dequant_2d(const void* q, const void* sb, const float* s_group, const int64_t* off,
+                                int64_t G, int64_t R, int64_t K, void* y, hipStream_t stream);
 }  // namespace bsq
 
 namespace {
@@ -244,6 +248,46 @@ int nv_dequantize_per_group(const void* q, const void* sb, const float* s_group,
     if (overlap(bufs, 5)) return BSQ_ERR_ALIAS;
     return hip_status(bsq::launch_nv_dequant_group(q, sb, s_group, group_offsets, G, R, K, y,
                                                    static_cast<hipStream_t>(stream)));
+}
+
+int nv_quantize_nvfp4_2d(const void* x, int64_t R, int64_t K, const int64_t* group_offsets, int64_t G,
+                         void* q, void* sb, float* s_group, int32_t* status_dev, void* stream) {
+    if (!size_ok(R, K, 2)) return BSQ_ERR_SHAPE;
+    if (R % 16 != 0 || K % 16 != 0) return BSQ_ERR_SHAPE;
+    if (G < 1 || G > INT64_MAX / 8 - 1) return BSQ_ERR_SHAPE;
+    if (group_offsets == nullptr || s_group == nullptr) return BSQ_ERR_NULL;
+    if (misaligned(group_offsets, 8) || misaligned(s_group, 16)) return BSQ_ERR_ALIGN;
+    if (status_dev != nullptr && misaligned(status_dev, 4)) return BSQ_ERR_ALIGN;
+    const bool empty = (R == 0 || K == 0);
+    if (!empty) {
+        if (x == nullptr || q == nullptr || sb == nullptr) return BSQ_ERR_NULL;
+        if (misaligned(x, 16) || misaligned(q, 16) || misaligned(sb, 16)) return BSQ_ERR_ALIGN;
+    }
+    const int64_t n = empty ? 0 : R * K;
+    const Buf bufs[6] = {{x, 2 * n}, {q, n / 2}, {sb, n / 256}, {s_group, 4 * G},
+                         {group_offsets, 8 * (G + 1)}, {status_dev, status_dev != nullptr ? 4 : 0}};
+    if (overlap(bufs, 6)) return BSQ_ERR_ALIAS;
+    return hip_status(bsq::launch_nv_quant_2d(x, R, K, group_offsets, G, q, sb, s_group, status_dev,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int nv_dequantize_2d(const void* q, const void* sb, const float* s_group, const int64_t* group_offsets,
+                     int64_t G, int64_t R, int64_t K, void* y, void* stream) {
+    if (!size_ok(R, K, 2)) return BSQ_ERR_SHAPE;
+    if (R % 16 != 0 || K % 16 != 0) return BSQ_ERR_SHAPE;
+    if (G < 1 || G > INT64_MAX / 8 - 1) return BSQ_ERR_SHAPE;
+    if (R == 0 || K == 0) return BSQ_OK;
+    if (q == nullptr || sb == nullptr || s_group == nullptr || group_offsets == nullptr || y == nullptr)
+        return BSQ_ERR_NULL;
+    if (misaligned(q, 16) || misaligned(sb, 16) || misaligned(s_group, 16) || misaligned(y, 16) ||
+        misaligned(group_offsets, 8))
+        return BSQ_ERR_ALIGN;
+    const int64_t n = R * K;
+    const Buf bufs[5] = {{q, n / 2}, {sb, n / 256}, {s_group, 4 * G}, {group_offsets, 8 * (G + 1)},
+                         {y, 2 * n}};
+    if (overlap(bufs, 5)) return BSQ_ERR_ALIAS;
+    return hip_status(bsq::launch_nv_dequant_2d(q, sb, s_group, group_offsets, G, R, K, y,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 int mx_dequantize(const void* q, const void* s, int64_t rows, int64_t cols, void* y,

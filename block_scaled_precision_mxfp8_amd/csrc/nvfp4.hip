@@ -70,10 +70,10 @@ __device__ __forceinline__ uint32_t nv_block_scale(uint32_t amax_b_bits, float s
 // Device-side check of the expert offsets of the grouped call, by one wave:
 // offsets[0] == 0, offsets[E] == R, offsets[e] <= offsets[e+1].
 __device__ void check_offsets(const int64_t* __restrict__ off, int64_t E, int64_t R,
-                              int32_t* __restrict__ status) {
+                              int32_t* __restrict__ status, int64_t gran = 1) {
     const int lane = threadIdx.x & 63;
     bool bad = false;
-    for (int64_t e = lane; e < E; e += 64) bad |= off[e] > off[e + 1];
+    for (int64_t e = lane; e < E; e += 64) bad |= off[e] > off[e + 1] || (off[e + 1] % gran) != 0;
     if (lane == 0) bad |= (off[0] != 0) || (off[E] != R);
     const bool any_bad = __any(bad);
     if (lane == 0) *status = any_bad ? 6 /* BSQ_ERR_OFFSETS */ : 0;
@@ -381,11 +381,9 @@ void nv_quant_scatter_long_kernel(const uint4* __restrict__ h, int64_t T, int64_
 // order is value order) in the caller's s_group array itself, which the last launch turns
 // into the scales in place.
 
-// Group offsets staged in LDS for the row -> group lookup (larger G searches in HBM).
-constexpr int NV_GROUP_LDS = 1024;
-
 // Group of row r: the g in [0, G) with off[g] <= r < off[g+1] (clamped into [0, G) so
-// that invalid offsets still index inside s_group).
+// that invalid offsets still index inside s_group).  Called with a wave-uniform row the
+// search runs on scalar loads, which the scalar cache serves after the first workgroup.
 __device__ __forceinline__ int64_t group_of(int64_t r, const int64_t* off, int64_t G) {
     int64_t lo = 0, hi = G;                           // off[lo] <= r < off[hi] (if valid)
     while (hi - lo > 1) {
@@ -395,21 +393,12 @@ __device__ __forceinline__ int64_t group_of(int64_t r, const int64_t* off, int64
     return lo;
 }
 
-// The workgroup's view of the offsets: the LDS copy when it fits, else the global array.
-__device__ __forceinline__ const int64_t* stage_offsets(const int64_t* __restrict__ off, int64_t G,
-                                                        int64_t* lds_off) {
-    if (G + 1 > NV_GROUP_LDS) return off;
-    for (int64_t i = threadIdx.x; i <= G; i += 64 * NV_WAVES) lds_off[i] = off[i];
-    __syncthreads();
-    return lds_off;
-}
-
 __global__ __launch_bounds__(256)
 void nv_group_init_kernel(uint32_t* __restrict__ amax_bits, int64_t G, const int64_t* __restrict__ off,
-                          int64_t R, int32_t* __restrict__ status) {
+                          int64_t R, int32_t* __restrict__ status, int64_t gran) {
     const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (g < G) amax_bits[g] = 0u;
-    if (status != nullptr && blockIdx.x == 0 && threadIdx.x < 64) check_offsets(off, G, R, status);
+    if (status != nullptr && blockIdx.x == 0 && threadIdx.x < 64) check_offsets(off, G, R, status, gran);
 }
 
 // Pass 1: group maxima.  Each wave streams a contiguous range of rows as one flat run of
@@ -424,8 +413,7 @@ __global__ __launch_bounds__(64 * NV_WAVES)
 void nv_group_amax_kernel(const uint4* __restrict__ x, int64_t R, int64_t K,
                           const int64_t* __restrict__ off, int64_t G, uint32_t* __restrict__ amax_bits,
                           int64_t rows_per_wave) {
-    __shared__ int64_t lds_off[NV_GROUP_LDS];
-    const int64_t* offs = stage_offsets(off, G, lds_off);
+    const int64_t* offs = off;
     const int lane = threadIdx.x & 63;
     const int64_t w = (int64_t)blockIdx.x * NV_WAVES + wave_id();
     int64_t r = w * rows_per_wave;
@@ -463,7 +451,6 @@ __global__ __launch_bounds__(64 * NV_WAVES)
 void nv_group_quant_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q, uint8_t* __restrict__ sb,
                            int64_t R, int64_t K, const int64_t* __restrict__ off, int64_t G,
                            const uint32_t* __restrict__ amax_bits) {
-    __shared__ int64_t lds_off[NV_GROUP_LDS];
     __shared__ __align__(16) uint8_t lds_sb[NV_WAVES][32 * NS];
     const int wave = wave_id();
     // workgroups in reverse row order: the first spans read are the rows the maximum pass
@@ -474,10 +461,9 @@ void nv_group_quant_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q
     const int n_ch = r0 >= R ? 0 : (RPW == 2 && r0 + 1 >= R) ? cpr : RPW * cpr;
     uint4 v[NS];
     if (n_ch > 0) load_span<NS, FULL>(v, x + r0 * cpr, n_ch);
-    const int64_t* offs = stage_offsets(off, G, lds_off);
     if (n_ch == 0) return;
-    const float s_a = nv_decode_scale(amax_bits[group_of(r0, offs, G)] >> 16);
-    const float s_b = (RPW == 2 && n_ch > cpr) ? nv_decode_scale(amax_bits[group_of(r0 + 1, offs, G)] >> 16) : 0.0f;
+    const float s_a = nv_decode_scale(amax_bits[group_of(r0, off, G)] >> 16);
+    const float s_b = (RPW == 2 && n_ch > cpr) ? nv_decode_scale(amax_bits[group_of(r0 + 1, off, G)] >> 16) : 0.0f;
     quant_span<NS, RPW, FULL>(v, r0, n_ch, cpr, s_a, s_b, q, sb, lds_sb[wave]);
 }
 
@@ -533,14 +519,12 @@ __global__ __launch_bounds__(64 * NV_WAVES)
 void nv_group_quant_long_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q, uint8_t* __restrict__ sb,
                                 int64_t R, int64_t K, const int64_t* __restrict__ off, int64_t G,
                                 const uint32_t* __restrict__ amax_bits) {
-    __shared__ int64_t lds_off[NV_GROUP_LDS];
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * NV_WAVES + (threadIdx.x >> 6);
-    const int64_t* offs = stage_offsets(off, G, lds_off);
     if (row >= R) return;
     const int64_t cpr = K >> 3;
     const uint4* xr = x + row * cpr;
-    const float s = nv_decode_scale(amax_bits[group_of(row, offs, G)] >> 16);
+    const float s = nv_decode_scale(amax_bits[group_of(row, off, G)] >> 16);
     const float p = 6.0f * s;
     uint32_t* qr = q + row * cpr;
     uint8_t* sbr = sb + row * (K >> 4);
@@ -555,6 +539,63 @@ void nv_group_quant_long_kernel(const uint4* __restrict__ x, uint32_t* __restric
             qr[ch] = packed;
             if ((lane & 1) == 0) sbr[ch >> 1] = (uint8_t)code;
         }
+    }
+}
+
+// ----------------------------------------------------------------------------- 16x16 tiles
+
+// NVFP4 with 16x16 weight tiles: two-dimensional block scaling of the weights, one of the
+// four parts of NVIDIA's NVFP4 pretraining recipe (page "NVIDIA verified the 4-bit NVFP4
+// format on a Mamba-Transformer (12B) at 10 trillion tokens"; Miles turns it off, "Towards
+// Blackwell-native 8-bit and 4-bit RL", section "Try the NVFP4 recipe in Miles").  Every
+// 16x16 tile shares one E4M3 scale under its row group's FP32 scale s_g (the group maxima
+// come from the per-group pass above), so one copy serves the weight and its transpose:
+//   sb = ENC_E4M3(fl(amax_tile / fl(6 s_g))),  f from sb as in the per-token steps,
+//   q = ENC_E2M1(fl(x f)).
+// One wave owns a strip of 16 rows x 256 columns: lane l = 32 h + c holds rows 8h .. 8h+7
+// of chunk column c (8 BF16 each), so a tile is the four lanes {2t, 2t+1, 32+2t, 33+2t}:
+// its maximum is a lane-local max, one DPP pair exchange and one exchange 32 lanes apart.
+// Each load instruction reads 512 contiguous bytes of two rows and each q store writes a
+// whole 128-byte line of two rows.
+constexpr int NV2D_COLS = 256;
+
+template <bool FULL>
+__global__ __launch_bounds__(64 * NV_WAVES)
+void nv_quant_2d_kernel(const uint16_t* __restrict__ x, uint32_t* __restrict__ q, uint8_t* __restrict__ sb,
+                        int64_t R, int64_t K, const int64_t* __restrict__ off, int64_t G,
+                        const uint32_t* __restrict__ amax_bits, int64_t col_strips) {
+    const int wave = wave_id();
+    const int lane = threadIdx.x & 63;
+    const int64_t strip = (int64_t)blockIdx.x * NV_WAVES + wave;
+    const int64_t n_strips = (R >> 4) * col_strips;
+    const int64_t rs = strip / col_strips;
+    const int64_t r0 = rs * 16;
+    const int64_t kw = (strip - rs * col_strips) * NV2D_COLS;
+    const int c = lane & 31, hrow = lane >> 5;
+    const int64_t col = kw + 8 * c;
+    const bool ok = FULL || col < K;
+    uint4 v[8];
+    if (strip < n_strips) {
+        const uint16_t* src = x + (r0 + 8 * hrow) * K + (ok ? col : kw);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = ld_stream<NVQ_NT_LOAD>(reinterpret_cast<const uint4*>(src + i * K));
+    }
+    if (strip >= n_strips) return;
+    const float s = nv_decode_scale(amax_bits[group_of(r0, off, G)] >> 16);
+    const float p = 6.0f * s;
+    uint32_t m = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = max(m, chunk_absmax8(v[i]));
+    m = pair_max(m);
+    m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+    float f;
+    const uint32_t code = nv_block_scale(m, s, p, f);
+    const int64_t cpr = K >> 3;
+    if (ok) {
+        uint32_t* qr = q + (r0 + 8 * hrow) * cpr + (col >> 3);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st_stream<NVQ_NT_STORE>(qr + i * cpr, nv_enc8(v[i], f));
+        if (hrow == 0 && (c & 1) == 0) sb[rs * (K >> 4) + (col >> 4)] = (uint8_t)code;
     }
 }
 
@@ -589,15 +630,21 @@ __device__ __forceinline__ uint32_t nv_dec2_nan(uint32_t word, float bscale, flo
 
 // GROUPED: st holds one scale per row group (offsets off[0..G], rows counted from row0);
 // each row's scale is that of its group.
-template <int NVDQ_SLOTS, bool GROUPED>
+template <int NVDQ_SLOTS, bool GROUPED, bool TWO_D = false>
 __global__ __launch_bounds__(256)
 void nv_dequant_kernel(const uint32_t* __restrict__ q, const uint8_t* __restrict__ sb,
                        const float* __restrict__ st, uint4* __restrict__ y,
                        uint32_t n_half, FastDiv halves_per_row,
                        const int64_t* __restrict__ off, int64_t G, int64_t row0) {
-    __shared__ int64_t lds_off[GROUPED ? NV_GROUP_LDS : 1];
-    const int64_t* offs = GROUPED ? stage_offsets(off, G, lds_off) : nullptr;
-    const int64_t g_first = GROUPED ? group_of(row0 + fastdiv(blockIdx.x * (256u * NVDQ_SLOTS), halves_per_row), offs, G) : 0;
+    // groups of the workgroup's first and last rows (uniform searches); the threads walk
+    // from the first one only when the workgroup straddles a group boundary
+    int64_t g_first = 0, g_last = 0;
+    if (GROUPED) {
+        const uint32_t h0 = blockIdx.x * (256u * NVDQ_SLOTS);
+        const uint32_t h1 = min(h0 + 256u * NVDQ_SLOTS, n_half) - 1u;
+        g_first = group_of(row0 + fastdiv(h0, halves_per_row), off, G);
+        g_last = group_of(row0 + fastdiv(h1, halves_per_row), off, G);
+    }
     const uint32_t base = blockIdx.x * (256u * NVDQ_SLOTS) + threadIdx.x;
     uint32_t w[NVDQ_SLOTS], code[NVDQ_SLOTS];
     float s_t[NVDQ_SLOTS];
@@ -606,12 +653,20 @@ void nv_dequant_kernel(const uint32_t* __restrict__ q, const uint8_t* __restrict
         const uint32_t h = base + 256u * j;
         const bool ok = h < n_half;
         w[j] = ok ? ld_stream<NVDQ_NT_LOAD>(q + h) : 0u;
-        code[j] = ok ? sb[h >> 1] : 0u;
+        if (TWO_D) {
+            // half block h = row r, columns 8 (h - r hpr) ..: tile (r / 16, (h - r hpr) / 2)
+            const uint32_t r = fastdiv(h, halves_per_row);
+            const uint32_t hpr = halves_per_row.d;
+            code[j] = ok ? sb[(uint64_t)(r >> 4) * (hpr >> 1) + ((h - r * hpr) >> 1)] : 0u;
+        } else {
+            code[j] = ok ? sb[h >> 1] : 0u;
+        }
         if (GROUPED) {
-            // rows of one workgroup span a few rows: walk from the group of its first row
-            const int64_t r = row0 + fastdiv(h, halves_per_row);
             int64_t g = g_first;
-            while (g + 1 < G && offs[g + 1] <= r) ++g;
+            if (g_last != g_first) {
+                const int64_t r = row0 + fastdiv(h, halves_per_row);
+                while (g < g_last && off[g + 1] <= r) ++g;
+            }
             s_t[j] = ok ? st[g] : 0.0f;
         }
         else s_t[j] = ok ? st[fastdiv(h, halves_per_row)] : 0.0f;
@@ -708,7 +763,8 @@ static hipError_t launch_nv_dequant_slots(const void* q, const void* sb, const f
         const int64_t rows = (R - r0 < rows_per_launch) ? R - r0 : rows_per_launch;
         const int64_t n_half = rows * hpr;
         const int64_t grid = (n_half + 256 * SLOTS - 1) / (256 * SLOTS);
-        hipLaunchKernelGGL((nv_dequant_kernel<SLOTS, GROUPED>), dim3((unsigned)grid), dim3(256), 0, stream,
+        hipLaunchKernelGGL((nv_dequant_kernel<SLOTS, GROUPED>), dim3((unsigned)grid), dim3(256),
+                           0, stream,
                            (const uint32_t*)q + r0 * hpr, (const uint8_t*)sb + r0 * (K / 16),
                            GROUPED ? st : st + r0, (uint4*)y + r0 * hpr, (uint32_t)n_half, div,
                            off, G, r0);
@@ -723,10 +779,11 @@ hipError_t launch_nv_dequant(const void* q, const void* sb, const float* st, int
     return launch_nv_dequant_slots<NV_DQ_SLOTS, false>(q, sb, st, R, K, y, nullptr, 0, stream);
 }
 
-// Slots per thread of the per-group dequant: each workgroup stages the offsets and finds
-// the group of its first row, so it takes more data than the per-token one.
+// Slots per thread of the per-group dequant (each workgroup first finds the groups of its
+// first and last rows).  Measured on the 128-expert weights: gate_up 212 / 167 / 178 us and
+// down 110 / 88 / 92 us with 2 / 4 / 8 slots.
 #ifndef BSQ_NV_DQ_GROUP_SLOTS
-#define BSQ_NV_DQ_GROUP_SLOTS 8
+#define BSQ_NV_DQ_GROUP_SLOTS 4
 #endif
 
 hipError_t launch_nv_dequant_group(const void* q, const void* sb, const float* s_group, const int64_t* off,
@@ -741,25 +798,71 @@ static void launch_group_passes(const void* x, int64_t R, int64_t K, void* q, vo
     const int64_t grid = (spans + NV_WAVES - 1) / NV_WAVES;
     const bool full = RPW * K == 512 * NS && R % RPW == 0;
     if (full)
-        hipLaunchKernelGGL((nv_group_quant_kernel<NS, RPW, true>), dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
-                           stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, R, K, off, G, bits);
+        hipLaunchKernelGGL((nv_group_quant_kernel<NS, RPW, true>), dim3((unsigned)grid), dim3(64 * NV_WAVES),
+                           0, stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, R, K, off, G, bits);
     else
-        hipLaunchKernelGGL((nv_group_quant_kernel<NS, RPW, false>), dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
-                           stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, R, K, off, G, bits);
+        hipLaunchKernelGGL((nv_group_quant_kernel<NS, RPW, false>), dim3((unsigned)grid), dim3(64 * NV_WAVES),
+                           0, stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, R, K, off, G, bits);
+}
+
+// Pass 1 of the per-group scales: about 8 waves per compute unit, each over a contiguous
+// range of rows.
+static void launch_group_amax(const void* x, int64_t R, int64_t K, const int64_t* off, int64_t G,
+                              uint32_t* bits, hipStream_t stream) {
+    const int64_t waves = 256 * 8 * NV_WAVES;
+    const int64_t rpw = (R + waves - 1) / waves;
+    const int64_t agrid = ((R + rpw - 1) / rpw + NV_WAVES - 1) / NV_WAVES;
+    hipLaunchKernelGGL(nv_group_amax_kernel, dim3((unsigned)agrid), dim3(64 * NV_WAVES),
+                       0, stream, (const uint4*)x, R, K, off, G, bits, rpw);
+}
+
+hipError_t launch_nv_quant_2d(const void* x, int64_t R, int64_t K, const int64_t* off, int64_t G,
+                              void* q, void* sb, float* s_group, int32_t* status, hipStream_t stream) {
+    uint32_t* bits = reinterpret_cast<uint32_t*>(s_group);
+    const unsigned gg = (unsigned)((G + 255) / 256);
+    hipLaunchKernelGGL(nv_group_init_kernel, dim3(gg), dim3(256), 0, stream, bits, G, off, R, status, (int64_t)16);
+    if (R > 0 && K > 0) {
+        launch_group_amax(x, R, K, off, G, bits, stream);
+        const int64_t col_strips = (K + NV2D_COLS - 1) / NV2D_COLS;
+        const int64_t strips = (R / 16) * col_strips;
+        const int64_t grid = (strips + NV_WAVES - 1) / NV_WAVES;
+        if (K % NV2D_COLS == 0)
+            hipLaunchKernelGGL(nv_quant_2d_kernel<true>, dim3((unsigned)grid), dim3(64 * NV_WAVES), 0, stream,
+                               (const uint16_t*)x, (uint32_t*)q, (uint8_t*)sb, R, K, off, G, bits, col_strips);
+        else
+            hipLaunchKernelGGL(nv_quant_2d_kernel<false>, dim3((unsigned)grid), dim3(64 * NV_WAVES), 0, stream,
+                               (const uint16_t*)x, (uint32_t*)q, (uint8_t*)sb, R, K, off, G, bits, col_strips);
+    }
+    hipLaunchKernelGGL(nv_group_finalize_kernel, dim3(gg), dim3(256), 0, stream, s_group, G);
+    return hipGetLastError();
+}
+
+hipError_t launch_nv_dequant_2d(const void* q, const void* sb, const float* s_group, const int64_t* off,
+                                int64_t G, int64_t R, int64_t K, void* y, hipStream_t stream) {
+    // 32-bit half-block indices: row ranges of fewer than 2^31 half blocks, whole tiles each
+    const int64_t hpr = K / 8;
+    const int64_t rows_per_launch = (((int64_t)1 << 31) / hpr) / 16 * 16;
+    const FastDiv div = make_fastdiv((uint32_t)hpr);
+    for (int64_t r0 = 0; r0 < R; r0 += rows_per_launch) {
+        const int64_t rows = (R - r0 < rows_per_launch) ? R - r0 : rows_per_launch;
+        const int64_t n_half = rows * hpr;
+        const int64_t grid = (n_half + 256 * BSQ_NV_DQ_GROUP_SLOTS - 1) / (256 * BSQ_NV_DQ_GROUP_SLOTS);
+        hipLaunchKernelGGL((nv_dequant_kernel<BSQ_NV_DQ_GROUP_SLOTS, true, true>), dim3((unsigned)grid), dim3(256),
+                           0, stream, (const uint32_t*)q + r0 * hpr, (const uint8_t*)sb + (r0 / 16) * (K / 16),
+                           s_group, (uint4*)y + r0 * hpr, (uint32_t)n_half, div, off, G, r0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_nv_quant_group(const void* x, int64_t R, int64_t K, const int64_t* off, int64_t G,
                                  void* q, void* sb, float* s_group, int32_t* status, hipStream_t stream) {
     uint32_t* bits = reinterpret_cast<uint32_t*>(s_group);   // group maxima, then the scales
     const unsigned gg = (unsigned)((G + 255) / 256);
-    hipLaunchKernelGGL(nv_group_init_kernel, dim3(gg), dim3(256), 0, stream, bits, G, off, R, status);
+    hipLaunchKernelGGL(nv_group_init_kernel, dim3(gg), dim3(256), 0, stream, bits, G, off, R, status, (int64_t)1);
     if (R > 0 && K > 0) {
-        // pass 1: about 8 waves per compute unit, each over a contiguous range of rows
-        const int64_t waves = 256 * 8 * NV_WAVES;
-        const int64_t rpw = (R + waves - 1) / waves;
-        const int64_t agrid = ((R + rpw - 1) / rpw + NV_WAVES - 1) / NV_WAVES;
-        hipLaunchKernelGGL(nv_group_amax_kernel, dim3((unsigned)agrid), dim3(64 * NV_WAVES), 0, stream,
-                           (const uint4*)x, R, K, off, G, bits, rpw);
+        launch_group_amax(x, R, K, off, G, bits, stream);
         if (K <= NV_PAIR_MAX_K) {
             switch ((2 * (K / 8) + 63) / 64) {
                 case 1: launch_group_passes<1, 2>(x, R, K, q, sb, bits, off, G, stream); break;
@@ -775,8 +878,8 @@ hipError_t launch_nv_quant_group(const void* x, int64_t R, int64_t K, const int6
                 case 7: case 8: launch_group_passes<8, 1>(x, R, K, q, sb, bits, off, G, stream); break;
                 default: {
                     const int64_t grid = (R + NV_WAVES - 1) / NV_WAVES;
-                    hipLaunchKernelGGL(nv_group_quant_long_kernel, dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
-                                       stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, R, K, off, G, bits);
+                    hipLaunchKernelGGL(nv_group_quant_long_kernel, dim3((unsigned)grid), dim3(64 * NV_WAVES),
+                                       0, stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, R, K, off, G, bits);
                 }
             }
         }

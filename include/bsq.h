@@ -197,6 +197,37 @@ int nv_dequantize_per_group(const void* q, const void* sb, const float* s_group,
                             void* y_bf16, void* stream);
 
 /*
+ * NVFP4 with 16x16 weight tiles (two-dimensional block scaling) under one FP32 scale per
+ * group of rows.  Passages: page "NVIDIA verified the 4-bit NVFP4 format on a
+ * Mamba-Transformer (12B) at 10 trillion tokens" (two-dimensional block scaling of the
+ * weights is one of the four parts of NVIDIA's pretraining recipe) and "Towards
+ * Blackwell-native 8-bit and 4-bit RL", section "Try the NVFP4 recipe in Miles" (Miles
+ * turns it off).  Square tiles make the codes and scales of the transposed weight the
+ * transposes of these, so one copy serves both GEMM orientations.
+ * Per group (as nv_quantize_nvfp4_per_group): s_g = fl(amax_g / 2688).  Per 16x16 tile:
+ *   sb = ENC_E4M3(fl(amax_tile / fl(6 s_g))); D = fl(DEC(sb) s_g);
+ *   f = 0 if D == 0 else min(fl(1/D), FLT_MAX);  q = ENC_E2M1(fl(x f)).
+ * Needs R % 16 == 0 and K % 16 == 0.  Outputs: q u8 [R][K/2] (packed as usual),
+ * sb u8 [R/16][K/16] (one byte per tile), s_group f32 [G] (DEVICE; it also holds the group
+ * maxima between the two passes).  group_offsets: DEVICE int64 [G+1], every one a multiple
+ * of 16, checked on the device into *status_dev (BSQ_ERR_OFFSETS / BSQ_OK) when it is not
+ * NULL; with invalid offsets the bytes are unspecified but stay inside the buffers.
+ */
+int nv_quantize_nvfp4_2d(const void* x_bf16, int64_t R, int64_t K,
+                         const int64_t* group_offsets, int64_t G,
+                         void* q, void* sb, float* s_group,
+                         int32_t* status_dev, void* stream);
+
+/*
+ * BF16 [R][K] from the 16x16-tile layout of nv_quantize_nvfp4_2d:
+ * y = RNE_BF16(fl(exact(DEC_E2M1(q) * DEC_E4M3(sb[r/16][c/16])) * s_g)); NaN -> 0x7FC0.
+ * Passage: "High-precision and dequantized backward".  Needs R % 16 == 0, K % 16 == 0.
+ */
+int nv_dequantize_2d(const void* q, const void* sb, const float* s_group,
+                     const int64_t* group_offsets, int64_t G, int64_t R, int64_t K,
+                     void* y_bf16, void* stream);
+
+/*
  * MXFP8 dequantization to BF16, in the stored layout: q u8 [rows][cols] E4M3 and
  * s u8 [rows][cols/32] E8M0 (blocks of 32 along the stored last dimension).
  * Passage: "High-precision and dequantized backward" (backward GEMMs consume BF16

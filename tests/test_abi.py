@@ -42,7 +42,8 @@ def _declared_functions():
 def test_header_declares_the_expected_entry_points():
     names = _declared_functions()
     for n in ("mx_quantize_mxfp8", "mx_quantize_mxfp8_grouped", "nv_quantize_nvfp4_per_group",
-              "nv_dequantize_per_group", "nv_quantize_nvfp4_per_token_scatter", "nv_quantize_nvfp4_per_token",
+              "nv_dequantize_per_group", "nv_quantize_nvfp4_per_token_scatter",
+              "nv_quantize_nvfp4_2d", "nv_dequantize_2d", "nv_quantize_nvfp4_per_token",
               "nv_quantize_nvfp4_per_token_grouped", "mx_dequantize", "nv_dequantize",
               "bsq_status_string", "bsq_abi_version"):
         assert n in names
@@ -188,6 +189,23 @@ def test_nv_per_group_validation(L):
     assert f(A, B, C, D + 4, 2, 4, 64, E_, None) == bsq.BSQ_ERR_ALIGN
     assert f(A, B, C, D, 2, 4, 64, A + 16, None) == bsq.BSQ_ERR_ALIAS
     assert f(A, B, C, D, 2, 0, 64, E_, None) == bsq.BSQ_OK
+
+
+def test_nv_2d_validation(L):
+    def f(x=A, R=32, K=64, off=E_, G=2, q=B, sb=C, s=D, status=None):
+        return L.nv_quantize_nvfp4_2d(x, R, K, off, G, q, sb, s, status, None)
+    assert f(R=24) == bsq.BSQ_ERR_SHAPE                        # R % 16
+    assert f(K=40) == bsq.BSQ_ERR_SHAPE
+    assert f(G=0) == bsq.BSQ_ERR_SHAPE
+    assert f(s=None) == bsq.BSQ_ERR_NULL
+    assert f(sb=None) == bsq.BSQ_ERR_NULL
+    assert f(sb=C + 8) == bsq.BSQ_ERR_ALIGN
+    assert f(sb=B + 16) == bsq.BSQ_ERR_ALIAS                   # tile scales inside q
+    d = L.nv_dequantize_2d
+    assert d(A, B, C, D, 2, 24, 64, E_, None) == bsq.BSQ_ERR_SHAPE
+    assert d(A, B, None, D, 2, 32, 64, E_, None) == bsq.BSQ_ERR_NULL
+    assert d(A, B, C, D, 2, 32, 64, A + 16, None) == bsq.BSQ_ERR_ALIAS
+    assert d(A, B, C, D, 2, 0, 64, E_, None) == bsq.BSQ_OK
 
 
 def test_nv_scatter_validation(L):

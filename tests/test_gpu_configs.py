@@ -109,6 +109,29 @@ def test_config4_weight_export_one_scale_per_expert():
         del q, sb, s, y
 
 
+def test_config4_weight_export_16x16_tiles():
+    """The 128 experts' weights with 16x16 tiles and one FP32 scale per expert tensor (gate
+    and up together).  Every output byte is compared."""
+    log("config4 2d: generating")
+    cfg = workloads.config4()
+    for key, rows in (("gate_up", 1536), ("down", 2048)):
+        w = cfg[key]
+        off = np.arange(0, w.shape[0] + 1, rows, dtype=np.int64)
+        offd = torch.from_numpy(off).cuda()
+        log("config4 %s: nvfp4 16x16" % key)
+        q, sb, s, status = bsq.nv_quantize_nvfp4_2d(to_dev(w), offd)
+        y = bsq.nv_dequantize_2d(q, sb, s, offd)
+        torch.cuda.synchronize()
+        assert int(status.item()) == bsq.BSQ_OK
+        eq, esb, es, ok = oracle.nv_quantize_2d(w, off)
+        assert ok
+        assert_same(key + " s_group", bits(s), es.view(np.uint32))
+        assert_same(key + " sb", bits(sb), esb)
+        assert_same(key + " q", bits(q), eq)
+        assert_same(key + " dequant", bits(y), oracle.nv_dequantize_2d(eq, esb, es, off))
+        del q, sb, s, y
+
+
 def test_config5_layer_step_stream():
     log("config5: generating")
     cfg = workloads.config5()
