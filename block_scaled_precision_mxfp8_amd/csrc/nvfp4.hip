@@ -401,47 +401,101 @@ void nv_group_init_kernel(uint32_t* __restrict__ amax_bits, int64_t G, const int
     if (status != nullptr && blockIdx.x == 0 && threadIdx.x < 64) check_offsets(off, G, R, status, gran);
 }
 
-// Pass 1: group maxima.  Each wave streams a contiguous range of rows as one flat run of
-// 16-byte chunks per group segment (rows end on chunk boundaries), keeps a lane-local
-// running maximum, and folds it into the group's maximum with one wave reduction and one
-// atomic per segment -- a few atomics per group instead of one per row.  Ordinary loads:
-// the quantize pass walks the tensor backwards and finds the last rows read here still
-// in the Infinity Cache.
-constexpr int NV_AMAX_UNROLL = 4;
+// Pass 1: group maxima.  The tensor is read as one flat run of 16-byte pieces (eight BF16
+// elements; a row holds K/8 of them) in a grid-stride sweep: at any moment the workgroups
+// read one contiguous band, each wave 64 lanes x NV_AMAX_PIECES neighbouring pieces.  The
+// band ends at the tensor's tail, which the quantize pass (walking backwards) then finds in
+// the Infinity Cache.  A wave's pieces nearly always lie in one group; a wave that straddles
+// group boundaries takes one masked maximum per group touched.  Maxima are kept as binary32
+// bits (non-negative, so unsigned order is value order).  With LDS_TABLE each workgroup
+// gathers its maxima in an LDS table of all G groups and sends each nonzero entry to the
+// global array with one atomicMax at its end: the waves in flight all work in the same few
+// groups, so an atomic per wave and piece run would serialise on those few addresses.
+// (Measured on the 128-expert weight stacks: 4 to 16 pieces a lane and 4 to 16 workgroups a
+// compute unit lie within 3% of each other; the sweep reads at about the pure-read rate.)
+#ifndef BSQ_NV_AMAX_PIECES
+#define BSQ_NV_AMAX_PIECES 8
+#endif
+#ifndef BSQ_NV_AMAX_WGS_PER_CU
+#define BSQ_NV_AMAX_WGS_PER_CU 4
+#endif
+constexpr int NV_AMAX_PIECES = BSQ_NV_AMAX_PIECES;
+constexpr int64_t NV_AMAX_LDS_GROUPS = 8192;          // 32 KiB of LDS per workgroup at most
 
+// Group of the piece p: largest g with off[g] * cpr <= p (clamped to [0, G)); uniform.
+__device__ __forceinline__ int64_t group_of_piece(int64_t p, const int64_t* off, int64_t G, int64_t cpr) {
+    int64_t lo = 0, hi = G;
+    while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (off[mid] * cpr <= p) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+template <bool LDS_TABLE>
+__device__ __forceinline__ void amax_put(uint32_t* table, uint32_t* amax_bits, int64_t g, uint32_t m, int lane) {
+    if (lane != 0) return;
+    if (LDS_TABLE) atomicMax(table + g, m << 16);
+    else atomicMax(amax_bits + g, m << 16);
+}
+
+template <bool LDS_TABLE>
 __global__ __launch_bounds__(64 * NV_WAVES)
 void nv_group_amax_kernel(const uint4* __restrict__ x, int64_t R, int64_t K,
-                          const int64_t* __restrict__ off, int64_t G, uint32_t* __restrict__ amax_bits,
-                          int64_t rows_per_wave) {
-    const int64_t* offs = off;
+                          const int64_t* __restrict__ off, int64_t G, uint32_t* __restrict__ amax_bits) {
+    extern __shared__ uint32_t table[];               // G entries when LDS_TABLE
+    constexpr int64_t WAVE_PIECES = 64 * NV_AMAX_PIECES;
     const int lane = threadIdx.x & 63;
-    const int64_t w = (int64_t)blockIdx.x * NV_WAVES + wave_id();
-    int64_t r = w * rows_per_wave;
-    const int64_t r_end = min(R, r + rows_per_wave);
-    if (r >= r_end) return;
     const int64_t cpr = K >> 3;
-    int64_t g = group_of(r, offs, G);
-    while (r < r_end) {
-        // rows r .. seg_end-1 lie in group g (clamped for invalid offsets)
-        int64_t seg_end = (g + 1 <= G) ? offs[g + 1] : r_end;
-        if (seg_end > r_end || g == G - 1) seg_end = r_end;
-        if (seg_end <= r) seg_end = r + 1;
-        const uint4* p = x + r * cpr;
-        const int64_t n = (seg_end - r) * cpr;
-        uint32_t m = 0u;
-        int64_t c = lane;
-        for (; c + 64 * (NV_AMAX_UNROLL - 1) < n; c += 64 * NV_AMAX_UNROLL) {
-            uint4 v[NV_AMAX_UNROLL];
+    const int64_t n = R * cpr;
+    const int64_t stride = (int64_t)gridDim.x * NV_WAVES * WAVE_PIECES;
+    if (LDS_TABLE) {
+        for (int64_t g = threadIdx.x; g < G; g += 64 * NV_WAVES) table[g] = 0u;
+        __syncthreads();
+    }
+    for (int64_t wb = ((int64_t)blockIdx.x * NV_WAVES + wave_id()) * WAVE_PIECES; wb < n; wb += stride) {
+        const int64_t we = min(n, wb + WAVE_PIECES);
+        uint32_t a[NV_AMAX_PIECES];
+        if (we - wb == WAVE_PIECES) {
+            uint4 v[NV_AMAX_PIECES];
 #pragma unroll
-            for (int u = 0; u < NV_AMAX_UNROLL; ++u) v[u] = p[c + 64 * u];
+            for (int u = 0; u < NV_AMAX_PIECES; ++u) v[u] = x[wb + 64 * u + lane];
 #pragma unroll
-            for (int u = 0; u < NV_AMAX_UNROLL; ++u) m = max(m, chunk_absmax8(v[u]));
+            for (int u = 0; u < NV_AMAX_PIECES; ++u) a[u] = chunk_absmax8(v[u]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < NV_AMAX_PIECES; ++u) {
+                const int64_t q = wb + 64 * u + lane;
+                a[u] = q < we ? chunk_absmax8(x[q]) : 0u;
+            }
         }
-        for (; c < n; c += 64) m = max(m, chunk_absmax8(p[c]));
-        m = wave_max(m);
-        if (lane == 0) atomicMax(amax_bits + g, m << 16);
-        r = seg_end;
-        if (r < r_end) g = group_of(r, offs, G);
+        const int64_t g0 = group_of_piece(wb, off, G, cpr);
+        const int64_t g1 = group_of_piece(we - 1, off, G, cpr);
+        if (g0 == g1) {
+            uint32_t m = a[0];
+#pragma unroll
+            for (int u = 1; u < NV_AMAX_PIECES; ++u) m = max(m, a[u]);
+            amax_put<LDS_TABLE>(table, amax_bits, g0, wave_max(m), lane);
+        } else {
+            for (int64_t g = g0; g <= g1; ++g) {       // g1 < g0 only for invalid offsets
+                const int64_t lo = g == g0 ? wb : off[g] * cpr;
+                const int64_t hi = g == g1 ? we : off[g + 1] * cpr;
+                uint32_t m = 0u;
+#pragma unroll
+                for (int u = 0; u < NV_AMAX_PIECES; ++u) {
+                    const int64_t q = wb + 64 * u + lane;
+                    if (q >= lo && q < hi) m = max(m, a[u]);
+                }
+                amax_put<LDS_TABLE>(table, amax_bits, g, wave_max(m), lane);
+            }
+        }
+    }
+    if (LDS_TABLE) {
+        __syncthreads();
+        for (int64_t g = threadIdx.x; g < G; g += 64 * NV_WAVES) {
+            const uint32_t m = table[g];
+            if (m != 0u) atomicMax(amax_bits + g, m);
+        }
     }
 }
 
@@ -805,15 +859,19 @@ static void launch_group_passes(const void* x, int64_t R, int64_t K, void* q, vo
                            0, stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, R, K, off, G, bits);
 }
 
-// Pass 1 of the per-group scales: about 8 waves per compute unit, each over a contiguous
-// range of rows.
+// Pass 1 of the per-group scales: a few workgroups per compute unit, grid-stride; the LDS
+// table of group maxima when G fits in it.
 static void launch_group_amax(const void* x, int64_t R, int64_t K, const int64_t* off, int64_t G,
                               uint32_t* bits, hipStream_t stream) {
-    const int64_t waves = 256 * 8 * NV_WAVES;
-    const int64_t rpw = (R + waves - 1) / waves;
-    const int64_t agrid = ((R + rpw - 1) / rpw + NV_WAVES - 1) / NV_WAVES;
-    hipLaunchKernelGGL(nv_group_amax_kernel, dim3((unsigned)agrid), dim3(64 * NV_WAVES),
-                       0, stream, (const uint4*)x, R, K, off, G, bits, rpw);
+    const int64_t per_wg = (int64_t)NV_WAVES * 64 * NV_AMAX_PIECES;
+    const int64_t need = (R * (K >> 3) + per_wg - 1) / per_wg;
+    const int64_t agrid = std::min<int64_t>(need, 256 * BSQ_NV_AMAX_WGS_PER_CU);
+    if (G <= NV_AMAX_LDS_GROUPS)
+        hipLaunchKernelGGL(nv_group_amax_kernel<true>, dim3((unsigned)agrid), dim3(64 * NV_WAVES),
+                           (size_t)G * sizeof(uint32_t), stream, (const uint4*)x, R, K, off, G, bits);
+    else
+        hipLaunchKernelGGL(nv_group_amax_kernel<false>, dim3((unsigned)agrid), dim3(64 * NV_WAVES), 0, stream,
+                           (const uint4*)x, R, K, off, G, bits);
 }
 
 hipError_t launch_nv_quant_2d(const void* x, int64_t R, int64_t K, const int64_t* off, int64_t G,
