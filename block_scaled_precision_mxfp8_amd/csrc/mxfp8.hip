@@ -539,6 +539,9 @@ constexpr int GROUP_BLOCKS = 4;
 #define BSQ_POLICY_MXGROUP_COL 0
 #endif
 constexpr bool MXGROUP_COL_NT = (BSQ_POLICY_MXGROUP_COL & 2) != 0;
+#ifndef BSQ_MXGROUP_COL_WINDOW
+#define BSQ_MXGROUP_COL_WINDOW 1
+#endif
 
 struct GroupTable {
     int64_t start[GROUP_BLOCKS];   // first row of each of the workgroup's blocks
@@ -732,6 +735,188 @@ void mx_quant_grouped_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t 
     }
 }
 
+// Line-owning variant, for the columnwise-only mode.  A workgroup owns a window of 128
+// rows (one 128-byte line of every q_col row it touches) and 256 columns, so no q_col line
+// is written by two workgroups: lines that two workgroups each fill in part cost far more
+// than their bytes (on the 524288 x 2048 routed rows, 128 Zipf-routed experts, the
+// block-quad kernel above takes 922 us columnwise against 620 us with 32-row aligned
+// segments; this one 686 and 622).  The blocks that overlap the window -- with segments of
+// 32 rows or more, four or five, the first and last possibly reaching outside it -- are
+// loaded whole (a block reaching outside is loaded by both neighbouring windows, mostly
+// from cache), and only the window's rows are stored.  The block's scale goes out from the
+// window that holds its first row.  Columnwise codes are gathered in LDS, one 128-byte
+// line (plus a 32-byte margin on each side) per column: every lane writes its 16 codes at
+// its rows' place -- first the lanes holding 1 to 15 rows of their block, slot by slot in
+// row order, then the lanes holding 16 -- so that where a lane's codes run past its
+// block's end (copies of the block's last row) the next block's codes overwrite them;
+// bytes that fall in the margins belong to the neighbouring windows and are dropped.  The
+// lines then leave as aligned 16-byte stores, eight lanes to a line.
+//
+// Wave layout: lane l = 4 rg + c holds rows 16 (rg & 1) .. + 15 of block slot rg >> 1 and
+// columns 8 c .. 8 c + 7 of the wave's 32; a 32x1 column block is the lane pair (rg,
+// rg ^ 1), lanes 4 apart (one swizzle).  A pass covers 8 block slots; a window overlapping
+// more blocks (segments shorter than 32 rows) takes more passes.  With the rowwise copy
+// too, the idle slots (3 of 8 for five blocks) and the edge rows loaded twice cost more
+// ALU and registers than the shared lines cost (dual, same rows: 1135 us against 1093),
+// so the dual mode stays on the block-quad kernel.
+constexpr int WIN_ROWS = 128;
+#ifndef BSQ_MXGROUP_WIN_WAVES
+#define BSQ_MXGROUP_WIN_WAVES 8
+#endif
+constexpr int WIN_WAVES = BSQ_MXGROUP_WIN_WAVES;       // 32 columns each
+constexpr int WIN_COLS = 32 * WIN_WAVES;
+constexpr int WIN_SLOTS = 8;                          // blocks per pass
+constexpr int WIN_TAB = WIN_ROWS;                     // each overlapping block holds a window row
+
+struct WindowTable {
+    int64_t start[WIN_TAB];        // first row of each overlapping block, in row order
+    int64_t n[WIN_TAB];            // its global block index
+    int32_t len[WIN_TAB];          // its row count (1..32); 0 for an unused entry
+    int32_t count;
+};
+
+// Wave 0: the blocks that overlap rows [w0, w0 + WIN_ROWS).  Offsets are clamped into
+// [0, M]; with invalid offsets entries may be missing (len 0), never out of bounds.
+__device__ void window_find_blocks(const int64_t* __restrict__ off, int64_t E, int64_t M, int64_t w0,
+                                   int64_t n_limit, WindowTable& tab) {
+    const int lane = threadIdx.x & 63;
+    const int64_t w1 = w0 + WIN_ROWS;
+    for (int i = lane; i < WIN_TAB; i += 64) { tab.start[i] = w0; tab.n[i] = 0; tab.len[i] = 0; }
+    int64_t base = 0;                                  // blocks of the experts before e0
+    int32_t slots = 0;                                 // table entries so far
+    for (int64_t e0 = 0; e0 < E; e0 += 64) {
+        if (clamp_row(off[e0], M) >= w1) break;        // uniform; later segments start past the window
+        const int64_t e = e0 + lane;
+        const int64_t lo = e < E ? clamp_row(off[e], M) : M;
+        const int64_t hi = e < E ? clamp_row(off[e + 1], M) : M;
+        const int32_t c = hi > lo ? (int32_t)((hi - lo + 31) >> 5) : 0;
+        const int32_t incl = wave_incl_scan(c);
+        const int64_t excl = base + (incl - c);
+        int32_t jf = 0, cnt = 0;
+        if (c > 0 && hi > w0 && lo < w1) {
+            jf = w0 > lo ? (int32_t)((w0 - lo) >> 5) : 0;
+            const int32_t jl = min(c - 1, (int32_t)((w1 - 1 - lo) >> 5));
+            cnt = max(jl - jf + 1, 0);
+        }
+        const int32_t sincl = wave_incl_scan(cnt);
+        const int32_t s0 = slots + (sincl - cnt);
+        for (int32_t k = 0; k < cnt; ++k) {
+            const int32_t sl = s0 + k;
+            const int64_t n = excl + jf + k;
+            if (sl < WIN_TAB && n < n_limit) {
+                const int64_t r = lo + 32 * (int64_t)(jf + k);   // < hi <= M
+                tab.start[sl] = r;
+                tab.n[sl] = n;
+                tab.len[sl] = (int32_t)(hi - r < 32 ? hi - r : 32);
+            }
+        }
+        base += __shfl(incl, 63, 64);
+        slots += __shfl(sincl, 63, 64);
+    }
+    if (lane == 0) tab.count = slots < WIN_TAB ? slots : WIN_TAB;
+}
+
+// Packed column maxima joined with the partner lane 4 apart (the other half of the block).
+__device__ __forceinline__ void win_join_pairs(uint32_t (&cm)[4]) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+        cm[d] = pk_absmax(cm[d], (uint32_t)__builtin_amdgcn_ds_swizzle((int)cm[d], 0x101F));  // lane ^ 4
+}
+
+__global__ __launch_bounds__(64 * WIN_WAVES)
+void mx_quant_grouped_col_window_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                        const int64_t* __restrict__ off, int64_t E,
+                                        uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col, int64_t s_ld,
+                                        int64_t n_limit, int64_t col_groups, int32_t* __restrict__ status) {
+    constexpr int CP = WIN_ROWS + 64;                 // column line + margins
+    __shared__ WindowTable tab;
+    __shared__ __align__(16) uint8_t lds_c[WIN_WAVES][32][CP];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t win = blockIdx.x / col_groups;
+    const int64_t kw = (blockIdx.x - win * col_groups) * WIN_COLS;
+    const int64_t w0 = win * WIN_ROWS;
+    if (wave == 0) window_find_blocks(off, E, M, w0, n_limit, tab);
+    if (wave == 1 && status != nullptr && blockIdx.x == 0) group_check(off, E, M, s_ld, status);
+    __syncthreads();
+    const int count = tab.count;
+
+    const int rg = lane >> 2, c = lane & 3;
+    const int slot = rg >> 1, half = rg & 1;
+    const int lcol = wave * 32 + 8 * c;
+    const int64_t col = kw + lcol;
+    const bool colok = col < K;
+    const uint16_t* xc = x + (colok ? col : kw);
+    for (int p = 0; p * WIN_SLOTS < count; ++p) {
+        const int sl = WIN_SLOTS * p + slot;
+        const int blen = sl < count ? tab.len[sl] : 0;
+        const int64_t bstart = blen > 0 ? tab.start[sl] : tab.start[WIN_SLOTS * p];   // a row inside the tensor
+        const int last = (blen > 0 ? blen : 1) - 1;
+        const int64_t r0 = bstart + 16 * half;        // lane's first row
+
+        uint4 v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int ri = min(16 * half + i, last);
+            v[i] = ld_stream<MXTILE_NT_LOAD>(reinterpret_cast<const uint4*>(xc + (bstart + ri) * K));
+        }
+        const int vc = min(max(blen - 16 * half, 0), 16);      // rows of this lane inside its block
+
+        uint32_t cm[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            uint32_t unused = 0u;
+            tile_row_chunk<false>(v[i], cm, unused);
+        }
+        win_join_pairs(cm);
+        const bool own_scale = blen > 0 && half == 0 && bstart >= w0 && colok;
+        const int64_t n = tab.n[sl < WIN_TAB ? sl : 0];
+        const int lo_c = 32 + (int)(r0 - w0);            // 1 .. 175: inside the margins
+        const bool any_part = __builtin_amdgcn_ballot_w64(vc > 0 && vc < 16) != 0;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint4 a, b;
+            uint32_t code0, code1;
+            tile_col_codes(v, cm[d], d, a, b, code0, code1);
+            uint8_t* la = &lds_c[wave][8 * c + 2 * d][lo_c];
+            if (any_part) {                            // lanes with 1..15 rows, in slot order
+#pragma unroll
+                for (int k = 0; k < WIN_SLOTS; ++k) {
+                    if (slot == k && vc > 0 && vc < 16) {
+                        __builtin_memcpy(la, &a, 16);
+                        __builtin_memcpy(la + CP, &b, 16);
+                    }
+                }
+            }
+            if (vc == 16) {                            // then the full lanes, over any overrun
+                __builtin_memcpy(la, &a, 16);
+                __builtin_memcpy(la + CP, &b, 16);
+            }
+            if (own_scale) {
+                s_col[(col + 2 * d) * s_ld + n] = (uint8_t)code0;
+                s_col[(col + 2 * d + 1) * s_ld + n] = (uint8_t)code1;
+            }
+        }
+    }
+    // the wave's 32 column lines: 16-byte chunk q of the wave is line q / 8, part q % 8
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (kw + wave * 32 < K) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int q = lane + 64 * t, cc = q >> 3, part = q & 7;
+            const int64_t row = w0 + 16 * part;
+            uint8_t* dst = q_col + (kw + wave * 32 + cc) * M + row;
+            const uint8_t* src = &lds_c[wave][cc][32 + 16 * part];
+            if (row + 16 <= M) {
+                st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(dst), *reinterpret_cast<const uint4*>(src));
+            } else {
+                for (int j = 0; row + j < M; ++j) dst[j] = src[j];
+            }
+        }
+    }
+}
+
 __global__ __launch_bounds__(64)
 void mx_group_check_kernel(const int64_t* __restrict__ off, int64_t E, int64_t M, int64_t s_ld,
                            int32_t* __restrict__ status) {
@@ -748,6 +933,14 @@ hipError_t launch_mx_quant_grouped(const void* x, int64_t M, int64_t K, int mode
     if (n_limit == 0 || K == 0) {
         if (status != nullptr)
             hipLaunchKernelGGL(mx_group_check_kernel, dim3(1), dim3(64), 0, stream, off, E, M, s_ld, status);
+        return hipGetLastError();
+    }
+    if (mode == 2 && BSQ_MXGROUP_COL_WINDOW) {
+        const int64_t col_groups = (K + WIN_COLS - 1) / WIN_COLS;
+        const int64_t grid = (M + WIN_ROWS - 1) / WIN_ROWS * col_groups;
+        hipLaunchKernelGGL(mx_quant_grouped_col_window_kernel, dim3((unsigned)grid), dim3(64 * WIN_WAVES), 0, stream,
+                           (const uint16_t*)x, M, K, off, E, (uint8_t*)q_col, (uint8_t*)s_col, s_ld, n_limit,
+                           col_groups, status);
         return hipGetLastError();
     }
     const int64_t col_groups = (K + 255) / 256;
