@@ -78,6 +78,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=1,
                    help="the CPU baseline runs 1/N of the step's rows")
+    p.add_argument("--cpu-reps", type=int, default=2,
+                   help="times the CPU baseline's sample is run inside its timed region "
+                        "(about 10 s of CPU work on a 16-core share at the defaults)")
     p.add_argument("--all-configs", action="store_true",
                    help="instead of the step: time every kernel of the five workloads on its own "
                         "(512 MiB cache flush before each launch) and print one JSON line per op")
@@ -213,7 +216,7 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(a_np, w_np, tok, args.cpu_sample)
+        out["cpu_baseline"] = cpu_baseline(a_np, w_np, tok, args.cpu_sample, args.cpu_reps)
 
     print(json.dumps(out), flush=True)
 
@@ -374,10 +377,10 @@ def all_configs(torch, bsq, workloads, dev, reps=21):
     torch.cuda.synchronize()
 
 
-def cpu_baseline(a_np, w_np, tok, frac):
-    """The CPU oracle (as it stands, OpenMP over rows) on 1/frac of the step's rows: the
-    first M/frac rows of A (both copies), the first rows of W, the first R/frac routed
-    rows, and the dequantization of all of those outputs."""
+def cpu_baseline(a_np, w_np, tok, frac, reps):
+    """The CPU oracle (as it stands, OpenMP over rows) on 1/frac of the step's rows, reps
+    times over: the first M/frac rows of A (both copies), the first rows of W, the first
+    R/frac routed rows, and the dequantization of all of those outputs."""
     import oracle
 
     MA = (a_np.shape[0] // frac) // 32 * 32
@@ -388,21 +391,22 @@ def cpu_baseline(a_np, w_np, tok, frac):
     x_s = a_np[tok[:RX]]
     oracle.lib()
     t0 = time.perf_counter()
-    for m in (a_s, w_s):
-        qr, sr = oracle.mx_quantize_rowwise(m)
-        qc, sc = oracle.mx_quantize_colwise(m)
-        oracle.mx_dequantize(qr, sr)
-        oracle.mx_dequantize(qc, sc)
-    q, sb, st = oracle.nv_quantize_per_token(x_s)
-    oracle.nv_dequantize(q, sb, st)
+    for _ in range(reps):
+        for m in (a_s, w_s):
+            qr, sr = oracle.mx_quantize_rowwise(m)
+            qc, sc = oracle.mx_quantize_colwise(m)
+            oracle.mx_dequantize(qr, sr)
+            oracle.mx_dequantize(qc, sc)
+        q, sb, st = oracle.nv_quantize_per_token(x_s)
+        oracle.nv_dequantize(q, sb, st)
     dt = time.perf_counter() - t0
     KA, KW, KX = a_s.shape[1], w_s.shape[1], x_s.shape[1]
-    b = (mx_both_bytes(MA, KA) + mx_both_bytes(MW, KW) + 2 * nv_bytes(RX, KX)
-         + 2 * mx_dq_bytes(MA, KA) + 2 * mx_dq_bytes(MW, KW))
+    b = reps * (mx_both_bytes(MA, KA) + mx_both_bytes(MW, KW) + 2 * nv_bytes(RX, KX)
+                + 2 * mx_dq_bytes(MA, KA) + 2 * mx_dq_bytes(MW, KW))
     return {"value": round(b / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.max_threads(),
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "1/%d of the step: A[:%d] and W[:%d] MXFP8 dual + dequant of both copies, "
-                      "%d routed rows NVFP4 + dequant" % (frac, MA, MW, RX)}
+            "sample": "%d x 1/%d of the step: A[:%d] and W[:%d] MXFP8 dual + dequant of both copies, "
+                      "%d routed rows NVFP4 + dequant" % (reps, frac, MA, MW, RX)}
 
 
 if __name__ == "__main__":
