@@ -82,6 +82,30 @@ def test_grouped_matches_oracle(name, M, K, off, mode):
         assert_same("s_col vs flat", s[:, :nb], fs)
 
 
+@pytest.mark.parametrize("mode", [bsq.MX_COLWISE, bsq.MX_BOTH])
+def test_grouped_more_than_2_pow_23_rows(mode):
+    """q_col past 2^31 bytes from its base with 1000 segments of random length (most not
+    multiples of 32): 64-bit addressing in both grouped kernels."""
+    M, K = (1 << 23) + 48, 32
+    log("mx grouped large %dx%d mode %d" % (M, K, mode))
+    rng = np.random.default_rng(29)
+    x = rng.integers(0, 1 << 16, size=(M, K), dtype=np.uint16)
+    x[(x & 0x7F80) == 0x7F80] &= 0xBFFF                       # finite inputs only
+    off = [0] + np.sort(rng.choice(np.arange(1, M), size=999, replace=False)).tolist() + [M]
+    nb = int(oracle.mx_group_blocks(off).sum())
+    qr, sr, qc, sc, status = _grouped_gpu(x, off, mode, nb)
+    assert status == bsq.BSQ_OK
+    eq, es, ok = oracle.mx_quantize_colwise_grouped(x, off)
+    assert ok
+    assert_same("q_col", qc.payload().reshape(K, M), eq)
+    assert_same("s_col", sc.payload().reshape(K, nb), es)
+    del eq, es
+    if mode == bsq.MX_BOTH:
+        eqr, esr = oracle.mx_quantize_rowwise(x)
+        assert_same("q_row", qr.payload().reshape(M, K), eqr)
+        assert_same("s_row", sr.payload().reshape(M, K // 32), esr)
+
+
 @pytest.mark.parametrize("off", [[1, 30, 64], [0, 40, 30, 64], [0, 30, 63], [0, 30, 70]],
                          ids=["first", "decreasing", "short_end", "long_end"])
 def test_grouped_reports_bad_offsets_and_stays_in_bounds(off):
