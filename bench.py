@@ -94,9 +94,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the quantizer path is row-local and this build runs "
-              "on a single MI355X (see DESIGN.md for how it would shard); --gpus %d is not "
-              "supported" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU: the quantizer path is row-local, so it would shard by "
+              "rows (each GPU quantizing its own rows and experts, with no communication) and is "
+              "measured on a single MI355X; --gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -10,7 +10,7 @@ Two implementations live here:
 * ``bsq_oracle.c`` -- plain C, OpenMP over rows, binary64 for exact steps and one C
   float operation for each step the contract rounds to binary32.  Wrapped below for
   numpy arrays.  This is the oracle the parity tests compare against.
-* ``exact.py`` -- exact-rational (``fractions.Fraction``) brute-force checker for tiny
+* ``exact.py`` -- exact-rational (``fractions.Fraction``) brute-force verifier for tiny
   inputs.  It pins the C oracle; it is never timed.
 
 Every function cites the passage of the pages it follows in ``bsq_oracle.c``.

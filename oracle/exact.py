@@ -1,4 +1,4 @@
-"""Exact-rational brute-force checker for the block-scaled quantizer contract.
+"""Exact-rational brute-force verifier for the block-scaled quantizer contract.
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  Used on tiny inputs to pin the C
 oracle; never timed.  It shares no code with ``bsq_oracle.c``: every value is a

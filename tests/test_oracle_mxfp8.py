@@ -85,7 +85,7 @@ def test_rowwise_differs_from_colwise_handmade_example():
     assert not np.array_equal(y_r, y_c.T)              # the two copies really differ
 
 
-# --------------------------------------------------------------------------- exact checker
+# --------------------------------------------------------------------------- exact verifier
 
 def _random_blocks(rng, n):
     """Blocks of the four kinds named on the pages: random, boundary, zeros, maxes."""
@@ -125,7 +125,7 @@ def _random_blocks(rng, n):
     return blocks
 
 
-def test_mx_oracle_matches_exact_checker_on_tiny_blocks():
+def test_mx_oracle_matches_exact_verifier_on_tiny_blocks():
     rng = np.random.default_rng(21)
     blocks = _random_blocks(rng, 240)
     x = np.stack(blocks).reshape(-1, 64)            # two blocks per row
@@ -294,7 +294,7 @@ def test_grouped_colwise_partial_block_equals_zero_padded_segment():
     assert blk == s.shape[1]
 
 
-def test_grouped_colwise_matches_exact_checker():
+def test_grouped_colwise_matches_exact_verifier():
     rng = np.random.default_rng(13)
     off = [0, 3, 3, 40, 41, 75]
     x = _rand_bf16(rng, off[-1], 4)

@@ -65,7 +65,7 @@ def test_handmade_row_matches_golden():
     assert np.array_equal(y[0], _bf16_exact(g["y"]))
 
 
-# --------------------------------------------------------------------------- exact checker
+# --------------------------------------------------------------------------- exact verifier
 
 def _rows_of_every_kind(rng, n, K):
     """Rows of the kinds the pages name for quantizer tests: random, boundary, zeros,
@@ -109,7 +109,7 @@ def _rows_of_every_kind(rng, n, K):
     return np.stack(rows)
 
 
-def test_nv_oracle_matches_exact_checker_on_tiny_rows():
+def test_nv_oracle_matches_exact_verifier_on_tiny_rows():
     rng = np.random.default_rng(31)
     x = _rows_of_every_kind(rng, 140, 32)
     q, sb, st = oracle.nv_quantize_per_token(x)
