@@ -716,9 +716,16 @@ void mx_quant_grouped_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t 
                     __builtin_memcpy(pb, &b, 16);
                 }
             } else {
-                const uint8_t* ba = reinterpret_cast<const uint8_t*>(&a);
-                const uint8_t* bb = reinterpret_cast<const uint8_t*>(&b);
-                for (int j = 0; j < vc; ++j) { pa[j] = ba[j]; pb[j] = bb[j]; }
+                // constant byte positions: a loop over vc bytes of the codes would index the
+                // registers at run time, which the compiler does through scratch memory (on
+                // every lane, full or not: 48 bytes a lane, about 10% of the kernel's time)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    if (j < vc) {
+                        pa[j] = (uint8_t)(dword_of(a, j >> 2) >> (8 * (j & 3)));
+                        pb[j] = (uint8_t)(dword_of(b, j >> 2) >> (8 * (j & 3)));
+                    }
+                }
             }
         }
         if (blen > 0) {
