@@ -512,14 +512,17 @@ static void launch_tile(const void* x, int64_t M, int64_t K, void* q_row, void* 
     }
 }
 
-// Geometry, tile order and persistent workgroup count used by the library (0 = one tile
-// per workgroup always; otherwise used once a tensor has more than twice as many tiles).
-// Measured on the 65536 x 2048 activations (dual, one launch after a 512 MiB read):
-// 1x4 row-band 105.6 us with 256 persistent workgroups, 106.2 us with one tile per
-// workgroup; 2x2 106.5, 1x8 108.2, 2x4 115.5; column-band order 138-170.  With the same
-// loads and stores and no arithmetic at all the pattern takes 102-113 us, and a plain
-// copy of the same byte count 93 us with these non-temporal stores, so the kernel runs
-// at the speed of its access pattern.
+// Geometry, tile order and persistent workgroup count used by the library for the
+// columnwise-only mode (0 = one tile per workgroup always; otherwise used once a tensor
+// has more than twice as many tiles); the dual mode always runs one tile per workgroup.
+// Measured on the 65536 x 2048 activations (dual, one launch after a 512 MiB read, before
+// the dual mode staged its columnwise codes in LDS): 1x4 row-band 105.6 us with 256
+// persistent workgroups, 106.2 us with one tile per workgroup; 2x2 106.5, 1x8 108.2, 2x4
+// 115.5; column-band order 138-170.  With the LDS staging the persistent form needs 208
+// VGPRs for its two tiles and one tile per workgroup is faster in the dual mode: 106.3 ->
+// 101.0 us (65536 x 2048), 325 -> 305 us (196608 x 2048), 882 -> 802 us (524288 x 2048),
+// and the layer step 6115 -> 6145 GB/s; the columnwise-only mode stays faster persistent
+// (78.6 against 81.3 us, 240 against 250 us).
 #ifndef BSQ_TILE_WR
 #define BSQ_TILE_WR 1
 #endif
@@ -1063,7 +1066,7 @@ hipError_t launch_mx_quant(const void* x, int64_t M, int64_t K, int mode,
         return hipGetLastError();
     }
     const int64_t n_wg = ((M + LibTile::ROWS - 1) / LibTile::ROWS) * ((K + LibTile::COLS - 1) / LibTile::COLS);
-    const int64_t pw = (n_wg > 2 * TILE_PERSISTENT_WGS) ? TILE_PERSISTENT_WGS : 0;
+    const int64_t pw = (mode == 2 && n_wg > 2 * TILE_PERSISTENT_WGS) ? TILE_PERSISTENT_WGS : 0;
     if (mode == 3)
         launch_tile<LibTile, true, TILE_ORDER>(x, M, K, q_row, s_row, q_col, s_col, stream, pw);
     else
