@@ -572,8 +572,9 @@ constexpr int GROUP_BLOCKS = 4;
 // Store policy of the columnwise codes (bit 1 = non-temporal).  Segments start at any row,
 // so the 128-byte lines of q_col at the edges of a workgroup's row range are shared with
 // the neighbouring workgroup; ordinary stores let the L2 merge them.  Measured on the
-// 524288 x 2048 routed rows (128 Zipf-routed experts, dual): 1096 us ordinary, 1450 us
-// non-temporal; with every segment a multiple of 32 rows, 871 us (the flat kernel: 899).
+// 524288 x 2048 routed rows (128 Zipf-routed experts, dual), each launch timed together
+// with the 512 MiB read after it (so that lines left dirty in the caches are paid for):
+// 984 us ordinary, 1489 us non-temporal; with one segment, 813 us (the flat kernel: 821).
 #ifndef BSQ_POLICY_MXGROUP_COL
 #define BSQ_POLICY_MXGROUP_COL 0
 #endif

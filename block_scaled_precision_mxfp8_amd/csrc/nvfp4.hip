@@ -267,6 +267,10 @@ void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
 // X, while reading H once instead of X (top_k times the bytes).  dst[t][j] is the routed
 // row of token t's j-th choice; a negative entry is a dropped choice, an entry >= N is
 // reported in *status and skipped.
+// Ordinary stores look faster for the scattered writes when the kernel is timed alone,
+// 172 -> 143 us on 65536 tokens x 2048 to top 8 of 128, but leave the dirty lines for
+// whatever runs next: timed together with the 512 MiB read that follows, 168 us with
+// non-temporal stores against 198 us with ordinary ones.
 
 __global__ __launch_bounds__(64)
 void nv_status_clear_kernel(int32_t* __restrict__ status) {
