@@ -106,12 +106,13 @@ def test_grouped_more_than_2_pow_23_rows(mode):
         assert_same("s_row", sr.payload().reshape(M, K // 32), esr)
 
 
+@pytest.mark.parametrize("mode", [bsq.MX_COLWISE, bsq.MX_BOTH])
 @pytest.mark.parametrize("off", [[1, 30, 64], [0, 40, 30, 64], [0, 30, 63], [0, 30, 70]],
                          ids=["first", "decreasing", "short_end", "long_end"])
-def test_grouped_reports_bad_offsets_and_stays_in_bounds(off):
+def test_grouped_reports_bad_offsets_and_stays_in_bounds(off, mode):
     M, K = 64, 64
     x = mixed_bf16(np.random.default_rng(7), M, K)
-    qr, sr, qc, sc, status = _grouped_gpu(x, off, bsq.MX_BOTH, 8)
+    qr, sr, qc, sc, status = _grouped_gpu(x, off, mode, 8)
     assert status == bsq.BSQ_ERR_OFFSETS
     for g in (qr, sr, qc, sc):
         g.payload()                                            # guard bytes intact
