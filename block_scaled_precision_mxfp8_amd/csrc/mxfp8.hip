@@ -117,9 +117,10 @@ void mx_quant_rowwise_kernel(const uint4* __restrict__ x, uint2* __restrict__ q,
 //    maximum is a lane-local packed max plus one DPP exchange between lanes 8 apart;
 //  * a 1x32 row block is the quad of lanes c = 4k .. 4k+3 of one row (DPP);
 //  * every load instruction reads 8 rows x 128 bytes (full lines);
-//  * the columnwise copy q_col[K][M] is written as one 16-byte store per lane and
-//    column (16 rows of E4M3), so the 8 lanes g = 0..7 fill 128 contiguous bytes of one
-//    q_col row: the transpose happens in registers and the writes stay coalesced;
+//  * the columnwise copy q_col[K][M] is encoded as 16 bytes per lane and column (16 rows
+//    of E4M3), so the 8 lanes g = 0..7 hold 128 contiguous bytes of one q_col row: the
+//    transpose happens in registers.  The columnwise-only mode stores them directly; the
+//    dual mode passes them through LDS first (see TILE_QCOL_LDS);
 //  * the rowwise codes of the whole workgroup tile are staged in LDS and leave as
 //    16-byte stores covering whole rows of the tile, so no store writes part of a line.
 // A workgroup is WR x WC wave tiles (TileGeom).  Scale codes are gathered in LDS and
