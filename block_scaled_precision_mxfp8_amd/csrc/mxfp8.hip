@@ -1094,9 +1094,18 @@ static void launch_mx_dequant_slots(const void* q, const void* s, int64_t rows, 
                        (const uint2*)q, (const uint8_t*)s, (uint4*)y, n_chunks);
 }
 
+// Tensors of up to MX_DQ_SMALL_CHUNKS chunks (8 codes each) take 8 slots per thread: a
+// quarter of the workgroups to dispatch and four times the loads in flight per wave.
+// Measured: 8192 x 2048 12.6 -> 11.9 us, 2048 x 6144 10.2 -> 9.2 us; at 196608 x 2048 two
+// slots stay faster (194 against 204 us), at 65536 x 2048 the two are level (67.0, 67.6).
+constexpr int64_t MX_DQ_SMALL_CHUNKS = int64_t(1) << 22;
+
 hipError_t launch_mx_dequant(const void* q, const void* s, int64_t rows, int64_t cols,
                              void* y, hipStream_t stream) {
-    launch_mx_dequant_slots<MX_DQ_SLOTS>(q, s, rows, cols, y, stream);
+    if (rows * cols / 8 <= MX_DQ_SMALL_CHUNKS)
+        launch_mx_dequant_slots<8>(q, s, rows, cols, y, stream);
+    else
+        launch_mx_dequant_slots<MX_DQ_SLOTS>(q, s, rows, cols, y, stream);
     return hipGetLastError();
 }
 
