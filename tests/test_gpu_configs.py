@@ -171,15 +171,13 @@ def test_config5_layer_step_stream():
     assert_same("A dequant col", bits(ya_c), oracle.mx_dequantize(*ec))
     del ec
 
-    log("config5: comparing sampled routed rows")
-    rows = np.sort(np.random.default_rng(55).choice(tok.size, 8192, replace=False))
-    rows_d = torch.from_numpy(rows).cuda()
-    x_s = a[tok[rows]]
-    eq, esb, est = oracle.nv_quantize_per_token(x_s)
-    assert_same("X st", bits(st.index_select(0, rows_d)), est.view(np.uint32))
-    assert_same("X sb", bits(sb.index_select(0, rows_d)), esb)
-    assert_same("X q", bits(q.index_select(0, rows_d)), eq)
-    assert_same("X dequant", bits(yx.index_select(0, rows_d)), oracle.nv_dequantize(eq, esb, est))
+    log("config5: comparing all 524288 routed rows")
+    eq, esb, est = oracle.nv_quantize_per_token(a[tok])
+    assert_same("X st", bits(st), est.view(np.uint32))
+    assert_same("X sb", bits(sb), esb)
+    assert_same("X q", bits(q), eq)
+    assert_same("X dequant", bits(yx), oracle.nv_dequantize(eq, esb, est))
+    del eq, esb, est
     # duplicated tokens (a token routed to 8 experts) give byte-identical rows
     first = {}
     for i, t in enumerate(tok[:4096]):
