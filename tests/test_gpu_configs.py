@@ -1,8 +1,8 @@
 """GPU parity at the full sizes of the five workloads (seeded synthetic inputs shaped like
 a Qwen3-30B-A3B-class MoE layer; recipes in workloads/__init__.py), with the same launch
-configuration the benchmark times.  Every output byte is compared with the CPU oracle,
-except the 524288 routed rows of the layer-step workload, which are compared on a
-seeded sample of rows (each row's NVFP4 bytes depend on that row only).
+configuration the benchmark times.  Every output byte is compared with the CPU oracle
+(the quantize-then-scatter rows against the grouped path on every byte, and against the
+oracle on a seeded sample of rows).
 """
 import numpy as np
 import pytest
