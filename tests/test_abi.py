@@ -259,3 +259,12 @@ def test_binding_refuses_cpu_tensors_without_calling_the_library():
         bsq.nv_quantize_nvfp4_per_token(x)
     with pytest.raises(ValueError):
         bsq.mx_quantize_mxfp8(x, "bogus")
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """No fallback: without the built library the binding raises instead of computing
+    anything another way."""
+    monkeypatch.setattr(bsq, "_lib", None)
+    monkeypatch.setattr(bsq, "LIB_PATH", str(tmp_path / "libbsq.so"))
+    with pytest.raises(ImportError, match="not built"):
+        bsq.lib()
