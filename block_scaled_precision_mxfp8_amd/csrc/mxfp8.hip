@@ -561,33 +561,14 @@ constexpr int TILE_PERSISTENT_WGS = BSQ_TILE_PERSISTENT_WGS;
 // q_col keeps the flat [K][M] layout and s_col[K][s_ld] holds block n at entry n of every
 // row.  The rowwise copy is row-local, identical to the flat one.
 //
-// A workgroup (4 waves side by side, 256 columns) takes 4 consecutive blocks, which cover
-// one contiguous range of at most 128 rows; one wave finds them with a scan of the
-// segment lengths.  The wave layout is the flat tile's: a lane pair owns one block (16
-// rows each); rows past the end of a partial block are loaded as copies of its last row,
-// which leaves the block maximum unchanged, and are not stored.  Columnwise codes go out
-// as one 16-byte store per lane and column (at any byte alignment: segments start at any
-// row) or byte stores for the part of a partial block.  Block indices are 32-bit
+// Two kernels, both owning 128-row windows of the rows (one 128-byte line of every q_col
+// row they touch): the columnwise-only mode takes a block-slot layout, the dual mode the
+// flat tile's layout with segmented block maxima.  Lines of q_col that two workgroups each
+// fill in part cost far more than their bytes: an earlier kernel that gave each workgroup
+// four consecutive blocks (and so split lines wherever segments start off a 32-row
+// boundary) took 980 us for the dual mode on 524288 x 2048 Zipf-routed rows, timed with the
+// write-back of the lines it left dirty, against 892 us now.  Block indices are 32-bit
 // (ceil(M/32) + E < 2^31, checked by the caller).
-constexpr int GROUP_BLOCKS = 4;
-// Store policy of the columnwise codes (bit 1 = non-temporal).  Segments start at any row,
-// so the 128-byte lines of q_col at the edges of a workgroup's row range are shared with
-// the neighbouring workgroup; ordinary stores let the L2 merge them.  Measured on the
-// 524288 x 2048 routed rows (128 Zipf-routed experts, dual), each launch timed together
-// with the 512 MiB read after it (so that lines left dirty in the caches are paid for):
-// 984 us ordinary, 1489 us non-temporal; with one segment, 813 us (the flat kernel: 821).
-#ifndef BSQ_POLICY_MXGROUP_COL
-#define BSQ_POLICY_MXGROUP_COL 0
-#endif
-constexpr bool MXGROUP_COL_NT = (BSQ_POLICY_MXGROUP_COL & 2) != 0;
-#ifndef BSQ_MXGROUP_COL_WINDOW
-#define BSQ_MXGROUP_COL_WINDOW 1
-#endif
-
-struct GroupTable {
-    int64_t start[GROUP_BLOCKS];   // first row of each of the workgroup's blocks
-    int32_t len[GROUP_BLOCKS];     // its row count (1..32), 0 past the last block
-};
 
 __device__ __forceinline__ int64_t clamp_row(int64_t r, int64_t M) { return r < 0 ? 0 : (r > M ? M : r); }
 
@@ -600,37 +581,6 @@ __device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
         if (lane >= o) v += u;
     }
     return v;
-}
-
-// Wave 0: locate blocks n0 .. n0+3 (block n exists if n < min(total, n_limit)).  Offsets
-// are clamped into [0, M] so that even invalid offsets never address outside the tensor.
-__device__ void group_find_blocks(const int64_t* __restrict__ off, int64_t E, int64_t M,
-                                  int64_t n0, int64_t n_limit, GroupTable& tab) {
-    const int lane = threadIdx.x & 63;
-    if (lane < GROUP_BLOCKS) { tab.start[lane] = 0; tab.len[lane] = 0; }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    int64_t base = 0;                                   // blocks of the experts before e0
-    for (int64_t e0 = 0; e0 < E && base < n0 + GROUP_BLOCKS; e0 += 64) {
-        const int64_t e = e0 + lane;
-        const int64_t lo = e < E ? clamp_row(off[e], M) : M;
-        const int64_t hi = e < E ? clamp_row(off[e + 1], M) : M;
-        const int32_t c = hi > lo ? (int32_t)((hi - lo + 31) >> 5) : 0;
-        const int32_t incl = wave_incl_scan(c);
-        const int64_t excl = base + (incl - c);
-#pragma unroll
-        for (int h = 0; h < GROUP_BLOCKS; ++h) {
-            const int64_t n = n0 + h;
-            if (c > 0 && n < n_limit && excl <= n && n < excl + c) {
-                const int64_t r = lo + 32 * (n - excl);
-                if (r < hi) {                            // always, unless the offsets are garbage
-                    tab.start[h] = r;
-                    tab.len[h] = (int32_t)(hi - r < 32 ? hi - r : 32);
-                }
-            }
-        }
-        base += __shfl(incl, 63, 64);
-    }
 }
 
 // Wave 0 of workgroup 0: offsets valid (o[0] = 0, non-decreasing, o[E] = M) and the
@@ -652,161 +602,25 @@ __device__ void group_check(const int64_t* __restrict__ off, int64_t E, int64_t 
     if (lane == 0) *status = any_bad ? 6 /* BSQ_ERR_OFFSETS */ : 0;
 }
 
-template <bool ROW>
-__global__ __launch_bounds__(256)
-void mx_quant_grouped_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
-                             const int64_t* __restrict__ off, int64_t E,
-                             uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
-                             uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col, int64_t s_ld,
-                             int64_t n_limit, int64_t col_groups, int32_t* __restrict__ status) {
-    using G = TileGeom<1, 4>;
-    __shared__ GroupTable tab;
-    __shared__ __align__(16) uint8_t lds_srow[G::ROWS][G::SROW_B];
-    __shared__ __align__(16) uint8_t lds_scol[G::COLS][GROUP_BLOCKS];
-    __shared__ __align__(16) uint8_t lds_q[ROW ? G::ROWS : 1][G::QPITCH];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t quad = blockIdx.x / col_groups;
-    const int64_t kw = (blockIdx.x - quad * col_groups) * G::COLS;
-    if (wave == 0) group_find_blocks(off, E, M, GROUP_BLOCKS * quad, n_limit, tab);
-    if (wave == 1 && status != nullptr && blockIdx.x == 0) group_check(off, E, M, s_ld, status);
-    __syncthreads();
-    if (tab.len[0] == 0) return;                       // uniform: no block left for this quad
-    const int64_t row0 = tab.start[0];                 // the quad's rows: row0 .. row0 + L - 1
-    int L = 0;
-#pragma unroll
-    for (int h = 0; h < GROUP_BLOCKS; ++h) L += tab.len[h];
-
-    const int g = lane >> 3, c = lane & 7;
-    const int h = g >> 1, half = g & 1;
-    const int lcol = wave * TILE_COLS + 8 * c;
-    const int64_t col = kw + lcol;
-    const bool colok = col < K;
-    const int blen = tab.len[h];
-    const int64_t bstart = blen > 0 ? tab.start[h] : row0;
-    const int vc = min(max(blen - 16 * half, 0), 16);  // rows of this lane inside its block
-    const int last = (blen > 0 ? blen : 1) - 1;        // last row of the block (offset)
-    const int pos0 = (int)(bstart - row0) + 16 * half; // lane's first row inside the quad's range
-
-    uint4 v[16];
-    {
-        const uint16_t* xc = x + (colok ? col : kw);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int ri = min(16 * half + i, last);
-            v[i] = ld_stream<MXTILE_NT_LOAD>(reinterpret_cast<const uint4*>(xc + (bstart + ri) * K));
-        }
-    }
-
-    uint32_t cm[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        uint32_t code = 0u;
-        const uint2 out = tile_row_chunk<ROW>(v[i], cm, code);
-        // (with valid offsets the quad's blocks are contiguous and 0 <= pos0 + i < 128;
-        //  the bound only keeps invalid offsets inside the staging buffer)
-        if (ROW && i < vc && (unsigned)(pos0 + i) < (unsigned)G::ROWS) {
-            *reinterpret_cast<uint2*>(&lds_q[pos0 + i][lcol]) = out;
-            lds_srow[pos0 + i][lcol >> 5] = (uint8_t)code;
-        }
-    }
-    if (ROW) tile_pin(v);
-
-    tile_join_pairs(cm);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        uint4 a, b;
-        uint32_t code0, code1;
-        tile_col_codes(v, cm[d], d, a, b, code0, code1);
-        if (colok && vc > 0) {
-            uint8_t* pa = q_col + (col + 2 * d) * M + bstart + 16 * half;
-            uint8_t* pb = pa + M;
-            if (vc == 16) {
-                if constexpr (MXGROUP_COL_NT) {
-                    typedef uint32_t u32x4u_t __attribute__((ext_vector_type(4), aligned(1)));
-                    __builtin_nontemporal_store(u32x4_t{a.x, a.y, a.z, a.w}, reinterpret_cast<u32x4u_t*>(pa));
-                    __builtin_nontemporal_store(u32x4_t{b.x, b.y, b.z, b.w}, reinterpret_cast<u32x4u_t*>(pb));
-                } else {
-                    __builtin_memcpy(pa, &a, 16);      // any byte alignment
-                    __builtin_memcpy(pb, &b, 16);
-                }
-            } else {
-                // constant byte positions: a loop over vc bytes of the codes would index the
-                // registers at run time, which the compiler does through scratch memory (on
-                // every lane, full or not: 48 bytes a lane, about 10% of the kernel's time)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    if (j < vc) {
-                        pa[j] = (uint8_t)(dword_of(a, j >> 2) >> (8 * (j & 3)));
-                        pb[j] = (uint8_t)(dword_of(b, j >> 2) >> (8 * (j & 3)));
-                    }
-                }
-            }
-        }
-        if (blen > 0) {
-            lds_scol[lcol + 2 * d][h] = (uint8_t)code0;     // the lane pair writes one value
-            lds_scol[lcol + 2 * d + 1][h] = (uint8_t)code1;
-        }
-    }
-    __syncthreads();
-
-    if (ROW) {
-        // rowwise codes of the quad's L rows, whole 256-byte row segments per store
-        constexpr int CHUNKS = G::COLS / 16;
-        for (int idx = threadIdx.x; idx < L * CHUNKS; idx += G::THREADS) {
-            const int r = idx / CHUNKS, c16 = idx % CHUNKS;
-            if (kw + 16 * c16 < K && row0 + r < M) {
-                const uint4 val = *reinterpret_cast<const uint4*>(&lds_q[r][16 * c16]);
-                st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(q_row + (row0 + r) * K + kw + 16 * c16), val);
-            }
-        }
-        const int64_t nb_row = K >> 5;
-        const int nb = (int)min((int64_t)G::SROW_B, nb_row - (kw >> 5));
-        for (int r = threadIdx.x; r < L && row0 + r < M; r += G::THREADS) {
-            uint8_t* dst = s_row + (row0 + r) * nb_row + (kw >> 5);
-            if (nb == G::SROW_B && (nb_row % G::SROW_B) == 0) store_scales<G::SROW_B>(dst, lds_srow[r]);
-            else for (int j = 0; j < nb; ++j) dst[j] = lds_srow[r][j];
-        }
-    }
-    // columnwise scales: blocks 4 quad .. of every column of the workgroup
-    {
-        int nblk = 0;
-#pragma unroll
-        for (int hh = 0; hh < GROUP_BLOCKS; ++hh) nblk += tab.len[hh] > 0 ? 1 : 0;
-        const int t = threadIdx.x;
-        if (kw + t < K) {
-            uint8_t* dst = s_col + (kw + t) * s_ld + GROUP_BLOCKS * quad;
-            if (nblk == GROUP_BLOCKS && (s_ld % GROUP_BLOCKS) == 0)
-                *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(lds_scol[t]);
-            else
-                for (int j = 0; j < nblk; ++j) dst[j] = lds_scol[t][j];
-        }
-    }
-}
-
-// Line-owning variant, for the columnwise-only mode.  A workgroup owns a window of 128
-// rows (one 128-byte line of every q_col row it touches) and 256 columns, so no q_col line
-// is written by two workgroups: lines that two workgroups each fill in part cost far more
-// than their bytes (on the 524288 x 2048 routed rows, 128 Zipf-routed experts, the
-// block-quad kernel above takes 922 us columnwise against 620 us with 32-row aligned
-// segments; this one 686 and 622).  The blocks that overlap the window -- with segments of
-// 32 rows or more, four or five, the first and last possibly reaching outside it -- are
-// loaded whole (a block reaching outside is loaded by both neighbouring windows, mostly
-// from cache), and only the window's rows are stored.  The block's scale goes out from the
-// window that holds its first row.  Columnwise codes are gathered in LDS, one 128-byte
-// line (plus a 32-byte margin on each side) per column: every lane writes its 16 codes at
-// its rows' place -- first the lanes holding 1 to 15 rows of their block, slot by slot in
-// row order, then the lanes holding 16 -- so that where a lane's codes run past its
-// block's end (copies of the block's last row) the next block's codes overwrite them;
-// bytes that fall in the margins belong to the neighbouring windows and are dropped.  The
-// lines then leave as aligned 16-byte stores, eight lanes to a line.
+// Columnwise-only mode.  A workgroup owns a window of 128 rows and 256 columns.  The blocks
+// that overlap the window -- with segments of 32 rows or more, four or five, the first and
+// last possibly reaching outside it -- are loaded whole (a block reaching outside is loaded
+// by both neighbouring windows, mostly from cache), and only the window's rows are stored.
+// The block's scale goes out from the window that holds its first row.  Columnwise codes
+// are gathered in LDS, one 128-byte line (plus a 32-byte margin on each side) per column:
+// every lane writes its 16 codes at its rows' place -- first the lanes holding 1 to 15 rows
+// of their block, slot by slot in row order, then the lanes holding 16 -- so that where a
+// lane's codes run past its block's end (copies of the block's last row) the next block's
+// codes overwrite them; bytes that fall in the margins belong to the neighbouring windows
+// and are dropped.  The lines then leave as aligned 16-byte stores, eight lanes to a line.
+// On the 524288 x 2048 routed rows: 686 us with 128 Zipf-routed experts, 602 us with one
+// segment (the flat columnwise kernel: 633 us); the dual kernel's segmented layout without
+// the rowwise copy measured 676 and 624 us.
 //
 // Wave layout: lane l = 4 rg + c holds rows 16 (rg & 1) .. + 15 of block slot rg >> 1 and
 // columns 8 c .. 8 c + 7 of the wave's 32; a 32x1 column block is the lane pair (rg,
 // rg ^ 1), lanes 4 apart (one swizzle).  A pass covers 8 block slots; a window overlapping
-// more blocks (segments shorter than 32 rows) takes more passes.  With the rowwise copy
-// too, the idle slots (3 of 8 for five blocks) and the edge rows loaded twice cost more
-// ALU and registers than the shared lines cost (dual, same rows: 1135 us against 1093),
-// so the dual mode stays on the block-quad kernel.
+// more blocks (segments shorter than 32 rows) takes more passes.
 constexpr int WIN_ROWS = 128;
 #ifndef BSQ_MXGROUP_WIN_WAVES
 #define BSQ_MXGROUP_WIN_WAVES 8
@@ -965,6 +779,297 @@ void mx_quant_grouped_col_window_kernel(const uint16_t* __restrict__ x, int64_t 
     }
 }
 
+// Dual mode with line ownership.  Same 128-row windows, with the flat tile's layout (lane
+// 8g + c holds window rows 16g .. 16g+15, columns 8c .. 8c+7 of its wave's 64), so every
+// lane works on rows of the window and the rowwise copy costs what it costs in the flat
+// kernel.  The 32x1 block maxima are segmented: each lane folds its rows into at most two
+// partial maxima (its rows meet at most two blocks when every block holds 16 rows or
+// more), the lanes with rows of the blocks that reach outside the window fold those rows
+// too, and the partial maxima meet in an LDS table of the window's blocks (ds_max per
+// column; each wave has its own table for its 64 columns, so only a wave barrier waits
+// for it).  Each row is then encoded with its own block's scale: the codes of a lane's
+// rows before and after its block boundary come from two converts and a byte select (one
+// convert when no lane of the wave has a boundary inside its rows).  The columnwise codes
+// leave as one 16-byte store per lane and column, eight lanes filling a q_col line.
+// Windows with more than DW_BLOCKS blocks, or with a block shorter than 16 rows, take the
+// block-slot path of the columnwise kernel instead (with the rowwise copy added).
+// Launched for three workgroups per compute unit (168 VGPRs; the compiler spills a few
+// 64-bit values, 32 bytes a lane, outside the per-row work): on the Zipf-routed rows
+// 892 us against 1010 us at two workgroups.
+constexpr int DW_BLOCKS = 8;
+
+// Bytes k of a 4-row group whose row 4u + k lies before the boundary b (t = b - 4u).
+__device__ __forceinline__ uint32_t split_mask(int t) {
+    return t <= 0 ? 0u : t >= 4 ? 0xFFFFFFFFu : (1u << (8 * t)) - 1u;
+}
+
+// Columnwise codes of dword d of the lane's 16 rows, rows [0, b) at the scales (sA0, sA1)
+// of columns 2d and 2d+1, rows [b, 16) at (sB0, sB1).
+__device__ __forceinline__ void tile_col_codes_split(const uint4 (&v)[16], int d, int b, float sA0, float sA1,
+                                                     float sB0, float sB1, uint4& a, uint4& bo) {
+    uint32_t ra[4], rb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint32_t r0w = dword_of(v[4 * u + 0], d), r1w = dword_of(v[4 * u + 1], d);
+        const uint32_t r2w = dword_of(v[4 * u + 2], d), r3w = dword_of(v[4 * u + 3], d);
+        const uint32_t pa0 = __builtin_amdgcn_perm(r1w, r0w, 0x05040100u);
+        const uint32_t pa1 = __builtin_amdgcn_perm(r3w, r2w, 0x05040100u);
+        const uint32_t pb0 = __builtin_amdgcn_perm(r1w, r0w, 0x07060302u);
+        const uint32_t pb1 = __builtin_amdgcn_perm(r3w, r2w, 0x07060302u);
+        const uint32_t aA = cvt_e4m3x4_into(pa0, pa0, pa1, sA0);
+        const uint32_t bA = cvt_e4m3x4_into(pb0, pb0, pb1, sA1);
+        if (b >= 16) { ra[u] = aA; rb[u] = bA; continue; }
+        const uint32_t m = split_mask(b - 4 * u);
+        const uint32_t aB = cvt_e4m3x4_into(pa1, pa0, pa1, sB0);
+        const uint32_t bB = cvt_e4m3x4_into(pb1, pb0, pb1, sB1);
+        ra[u] = (aA & m) | (aB & ~m);
+        rb[u] = (bA & m) | (bB & ~m);
+    }
+    a = make_uint4(ra[0], ra[1], ra[2], ra[3]);
+    bo = make_uint4(rb[0], rb[1], rb[2], rb[3]);
+}
+
+// The 8 column maxima of a lane (packed pairs) into row j of the block table.
+__device__ __forceinline__ void dw_put(uint32_t (*bmax)[TILE_COLS], int j, int lcol, const uint32_t (&cm)[4]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t m = (e & 1) ? (cm[e >> 1] >> 16) : (cm[e >> 1] & 0xFFFFu);
+        if (m != 0u) atomicMax(&bmax[j][lcol + e], m);
+    }
+}
+
+typedef uint32_t u32x4u_t __attribute__((ext_vector_type(4), aligned(1)));
+
+__global__ __launch_bounds__(256, 3)
+void mx_quant_grouped_dual_window_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                         const int64_t* __restrict__ off, int64_t E,
+                                         uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
+                                         uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col, int64_t s_ld,
+                                         int64_t n_limit, int64_t col_groups, int32_t* __restrict__ status) {
+    using G = TileGeom<1, 4>;                          // 128 rows x 256 columns, 4 waves
+    __shared__ WindowTable tab;
+    __shared__ __align__(16) uint8_t lds_srow[G::ROWS][G::SROW_B];
+    __shared__ __align__(16) uint8_t lds_q[G::ROWS][G::QPITCH];
+    __shared__ uint32_t bmax_w[4][DW_BLOCKS][TILE_COLS];       // per wave: its 64 columns
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t win = blockIdx.x / col_groups;
+    const int64_t kw = (blockIdx.x - win * col_groups) * G::COLS;
+    const int64_t w0 = win * WIN_ROWS, w1 = w0 + WIN_ROWS;
+    if (wave == 0) window_find_blocks(off, E, M, w0, n_limit, tab);
+    if (wave == 1 && status != nullptr && blockIdx.x == 0) group_check(off, E, M, s_ld, status);
+    __syncthreads();
+    const int count = tab.count;
+    bool fast = count >= 1 && count <= DW_BLOCKS;
+    for (int j = 0; j < count && fast; ++j) fast = tab.len[j] >= 16;   // uniform
+
+    if (fast) {
+        const int g = lane >> 3, c = lane & 7;
+        const int lcol = wave * TILE_COLS + 8 * c;
+        const int64_t col = kw + lcol;
+        const bool colok = col < K;
+        const uint16_t* xc = x + (colok ? col : kw);
+        uint32_t (*bmax)[TILE_COLS] = bmax_w[wave];
+        const int wcol = 8 * c;                        // the lane's first column in the wave
+#pragma unroll
+        for (int i = 0; i < DW_BLOCKS; ++i) bmax[i][lane] = 0u;
+        const int64_t r0 = w0 + 16 * g;                // the lane's first row
+        const int hi = (int)max<int64_t>(min<int64_t>(M - r0, 16), 0);   // its rows inside the tensor
+        // rows of the blocks that reach outside the window: 4 before and 4 after it a lane,
+        // folded before the window rows are loaded (fewer registers live at once)
+        const int64_t hs = tab.start[0];               // head block, if it starts before w0
+        const int64_t te = tab.start[count - 1] + tab.len[count - 1];   // tail block's end
+        const bool head = hs < w0, tail = te > w1;     // uniform
+        uint32_t ch[4] = {0u, 0u, 0u, 0u}, ct[4] = {0u, 0u, 0u, 0u};
+        if (head || tail) {
+            uint4 eh[4], et[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int64_t rh = w0 - 32 + 4 * g + t, rt = w1 + 4 * g + t;
+                eh[t] = ld_stream<MXTILE_NT_LOAD>(reinterpret_cast<const uint4*>(xc + (head && rh >= hs ? rh : w0) * K));
+                et[t] = ld_stream<MXTILE_NT_LOAD>(reinterpret_cast<const uint4*>(xc + (tail && rt < te ? rt : w0) * K));
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const bool vh = head && w0 - 32 + 4 * g + t >= hs, vt = tail && w1 + 4 * g + t < te;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    ch[d] = vh ? pk_absmax(ch[d], dword_of(eh[t], d) & 0x7FFF7FFFu) : ch[d];
+                    ct[d] = vt ? pk_absmax(ct[d], dword_of(et[t], d) & 0x7FFF7FFFu) : ct[d];
+                }
+            }
+        }
+        uint4 v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            v[i] = ld_stream<MXTILE_NT_LOAD>(reinterpret_cast<const uint4*>(xc + (i < hi ? r0 + i : w0) * K));
+        // rowwise codes, staged in LDS
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            uint32_t code = 0u, unused[4] = {0u, 0u, 0u, 0u};
+            const uint2 out = tile_row_chunk<true>(v[i], unused, code);
+            if (i < hi) {
+                *reinterpret_cast<uint2*>(&lds_q[16 * g + i][lcol]) = out;
+                lds_srow[16 * g + i][lcol >> 5] = (uint8_t)code;
+            }
+        }
+        tile_pin(v);
+        // the lane's blocks: ja holds rows [0, b), ja + 1 rows [b, hi)
+        int ja = 0;
+        for (int j = 1; j < count; ++j) ja = tab.start[j] <= r0 ? j : ja;
+        const int jb = ja + 1 < count ? ja + 1 : ja;
+        const int b = ja + 1 < count ? (int)max<int64_t>(min<int64_t>(tab.start[ja + 1] - r0, 16), 0) : 16;
+        uint32_t ca[4] = {0u, 0u, 0u, 0u}, cb[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const bool in_a = i < b && i < hi, in_b = i >= b && i < hi;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t m = dword_of(v[i], d) & 0x7FFF7FFFu;
+                ca[d] = in_a ? pk_absmax(ca[d], m) : ca[d];
+                cb[d] = in_b ? pk_absmax(cb[d], m) : cb[d];
+            }
+        }
+        if (hi > 0) dw_put(bmax, ja, wcol, ca);
+        if (b < hi) dw_put(bmax, jb, wcol, cb);
+        if (head) dw_put(bmax, 0, wcol, ch);
+        if (tail) dw_put(bmax, count - 1, wcol, ct);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // the wave's own table
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // scales of the lane's two blocks, column codes, stores
+        uint32_t codeA[8], codeB[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            codeA[e] = mx_code(bmax[ja][wcol + e]);
+            codeB[e] = mx_code(bmax[jb][wcol + e]);
+        }
+        const bool own_a = hi > 0 && tab.start[ja] == r0 && colok;   // block ja starts at row r0
+        const bool own_b = b < hi && colok;                           // block jb starts inside
+        const int64_t na = tab.n[ja], nb = tab.n[jb];
+        const bool one_block = __builtin_amdgcn_ballot_w64(b < hi) == 0;   // no lane of the wave splits
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint4 a, bo;
+            if (one_block)
+                tile_col_codes_split(v, d, 16, mx_scale(codeA[2 * d]), mx_scale(codeA[2 * d + 1]),
+                                     mx_scale(codeA[2 * d]), mx_scale(codeA[2 * d + 1]), a, bo);
+            else
+                tile_col_codes_split(v, d, b, mx_scale(codeA[2 * d]), mx_scale(codeA[2 * d + 1]),
+                                     mx_scale(codeB[2 * d]), mx_scale(codeB[2 * d + 1]), a, bo);
+            if (colok && hi > 0) {
+                uint8_t* pa = q_col + (col + 2 * d) * M + r0;
+                uint8_t* pb = pa + M;
+                if (hi == 16) {
+                    __builtin_nontemporal_store(u32x4_t{a.x, a.y, a.z, a.w}, reinterpret_cast<u32x4u_t*>(pa));
+                    __builtin_nontemporal_store(u32x4_t{bo.x, bo.y, bo.z, bo.w}, reinterpret_cast<u32x4u_t*>(pb));
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        if (j < hi) {
+                            pa[j] = (uint8_t)(dword_of(a, j >> 2) >> (8 * (j & 3)));
+                            pb[j] = (uint8_t)(dword_of(bo, j >> 2) >> (8 * (j & 3)));
+                        }
+                    }
+                }
+            }
+            if (own_a) {
+                s_col[(col + 2 * d) * s_ld + na] = (uint8_t)codeA[2 * d];
+                s_col[(col + 2 * d + 1) * s_ld + na] = (uint8_t)codeA[2 * d + 1];
+            }
+            if (own_b) {
+                s_col[(col + 2 * d) * s_ld + nb] = (uint8_t)codeB[2 * d];
+                s_col[(col + 2 * d + 1) * s_ld + nb] = (uint8_t)codeB[2 * d + 1];
+            }
+        }
+    } else {
+        // block-slot path: lane 4 rg + c, 32 columns at a time (two halves of the wave's 64)
+        const int rg = lane >> 2, c = lane & 3;
+        const int slot = rg >> 1, half = rg & 1;
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int lcol = wave * TILE_COLS + 32 * h2 + 8 * c;
+            const int64_t col = kw + lcol;
+            const bool colok = col < K;
+            const uint16_t* xc = x + (colok ? col : kw);
+            for (int p = 0; p * WIN_SLOTS < count; ++p) {
+                const int sl = WIN_SLOTS * p + slot;
+                const int blen = sl < count ? tab.len[sl] : 0;
+                const int64_t bstart = blen > 0 ? tab.start[sl] : tab.start[WIN_SLOTS * p];
+                const int last = (blen > 0 ? blen : 1) - 1;
+                const int64_t r0 = bstart + 16 * half;
+                uint4 v[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int ri = min(16 * half + i, last);
+                    v[i] = ld_stream<MXTILE_NT_LOAD>(reinterpret_cast<const uint4*>(xc + (bstart + ri) * K));
+                }
+                const int vc = min(max(blen - 16 * half, 0), 16);
+                const int ilo = (int)max<int64_t>(w0 - r0, 0);
+                const int ihi = (int)min<int64_t>(w1 - r0, (int64_t)vc);
+                uint32_t cm[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    uint32_t code = 0u;
+                    const uint2 out = tile_row_chunk<true>(v[i], cm, code);
+                    if (i >= ilo && i < ihi) {
+                        const int wr = (int)(r0 - w0) + i;             // 0 <= wr < WIN_ROWS
+                        *reinterpret_cast<uint2*>(&lds_q[wr][lcol]) = out;
+                        lds_srow[wr][lcol >> 5] = (uint8_t)code;
+                    }
+                }
+                tile_pin(v);
+                win_join_pairs(cm);
+                const bool own_scale = blen > 0 && half == 0 && bstart >= w0 && colok;
+                const int64_t n = tab.n[sl < WIN_TAB ? sl : 0];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    uint4 a, bo;
+                    uint32_t code0, code1;
+                    tile_col_codes(v, cm[d], d, a, bo, code0, code1);
+                    if (colok && ihi > ilo) {
+                        uint8_t* pa = q_col + (col + 2 * d) * M + r0;
+                        uint8_t* pb = pa + M;
+                        if (ilo == 0 && ihi == 16) {
+                            __builtin_memcpy(pa, &a, 16);
+                            __builtin_memcpy(pb, &bo, 16);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < 16; ++j) {
+                                if (j >= ilo && j < ihi) {
+                                    pa[j] = (uint8_t)(dword_of(a, j >> 2) >> (8 * (j & 3)));
+                                    pb[j] = (uint8_t)(dword_of(bo, j >> 2) >> (8 * (j & 3)));
+                                }
+                            }
+                        }
+                    }
+                    if (own_scale) {
+                        s_col[(col + 2 * d) * s_ld + n] = (uint8_t)code0;
+                        s_col[(col + 2 * d + 1) * s_ld + n] = (uint8_t)code1;
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // rowwise codes and scales of the window's rows
+    const int L = (int)min<int64_t>(WIN_ROWS, M - w0);
+    constexpr int CHUNKS = G::COLS / 16;
+    for (int idx = threadIdx.x; idx < L * CHUNKS; idx += G::THREADS) {
+        const int r = idx / CHUNKS, c16 = idx % CHUNKS;
+        if (kw + 16 * c16 < K) {
+            const uint4 val = *reinterpret_cast<const uint4*>(&lds_q[r][16 * c16]);
+            st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(q_row + (w0 + r) * K + kw + 16 * c16), val);
+        }
+    }
+    const int64_t nb_row = K >> 5;
+    const int nbr = (int)min((int64_t)G::SROW_B, nb_row - (kw >> 5));
+    for (int r = threadIdx.x; r < L; r += G::THREADS) {
+        uint8_t* dst = s_row + (w0 + r) * nb_row + (kw >> 5);
+        if (nbr == G::SROW_B && (nb_row % G::SROW_B) == 0) store_scales<G::SROW_B>(dst, lds_srow[r]);
+        else for (int j = 0; j < nbr; ++j) dst[j] = lds_srow[r][j];
+    }
+}
+
 __global__ __launch_bounds__(64)
 void mx_group_check_kernel(const int64_t* __restrict__ off, int64_t E, int64_t M, int64_t s_ld,
                            int32_t* __restrict__ status) {
@@ -983,25 +1088,19 @@ hipError_t launch_mx_quant_grouped(const void* x, int64_t M, int64_t K, int mode
             hipLaunchKernelGGL(mx_group_check_kernel, dim3(1), dim3(64), 0, stream, off, E, M, s_ld, status);
         return hipGetLastError();
     }
-    if (mode == 2 && BSQ_MXGROUP_COL_WINDOW) {
+    if (mode == 3) {
+        const int64_t col_groups = (K + 255) / 256;
+        const int64_t grid = (M + WIN_ROWS - 1) / WIN_ROWS * col_groups;
+        hipLaunchKernelGGL(mx_quant_grouped_dual_window_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                           (const uint16_t*)x, M, K, off, E, (uint8_t*)q_row, (uint8_t*)s_row,
+                           (uint8_t*)q_col, (uint8_t*)s_col, s_ld, n_limit, col_groups, status);
+    } else {
         const int64_t col_groups = (K + WIN_COLS - 1) / WIN_COLS;
         const int64_t grid = (M + WIN_ROWS - 1) / WIN_ROWS * col_groups;
         hipLaunchKernelGGL(mx_quant_grouped_col_window_kernel, dim3((unsigned)grid), dim3(64 * WIN_WAVES), 0, stream,
                            (const uint16_t*)x, M, K, off, E, (uint8_t*)q_col, (uint8_t*)s_col, s_ld, n_limit,
                            col_groups, status);
-        return hipGetLastError();
     }
-    const int64_t col_groups = (K + 255) / 256;
-    const int64_t quads = (n_limit + GROUP_BLOCKS - 1) / GROUP_BLOCKS;
-    const int64_t grid = quads * col_groups;
-    if (mode == 3)
-        hipLaunchKernelGGL(mx_quant_grouped_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream,
-                           (const uint16_t*)x, M, K, off, E, (uint8_t*)q_row, (uint8_t*)s_row,
-                           (uint8_t*)q_col, (uint8_t*)s_col, s_ld, n_limit, col_groups, status);
-    else
-        hipLaunchKernelGGL(mx_quant_grouped_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream,
-                           (const uint16_t*)x, M, K, off, E, nullptr, nullptr,
-                           (uint8_t*)q_col, (uint8_t*)s_col, s_ld, n_limit, col_groups, status);
     return hipGetLastError();
 }
 
