@@ -561,14 +561,13 @@ constexpr int TILE_PERSISTENT_WGS = BSQ_TILE_PERSISTENT_WGS;
 // q_col keeps the flat [K][M] layout and s_col[K][s_ld] holds block n at entry n of every
 // row.  The rowwise copy is row-local, identical to the flat one.
 //
-// Two kernels, both owning 128-row windows of the rows (one 128-byte line of every q_col
-// row they touch): the columnwise-only mode takes a block-slot layout, the dual mode the
-// flat tile's layout with segmented block maxima.  Lines of q_col that two workgroups each
-// fill in part cost far more than their bytes: an earlier kernel that gave each workgroup
-// four consecutive blocks (and so split lines wherever segments start off a 32-row
-// boundary) took 980 us for the dual mode on 524288 x 2048 Zipf-routed rows, timed with the
-// write-back of the lines it left dirty, against 892 us now.  Block indices are 32-bit
-// (ceil(M/32) + E < 2^31, checked by the caller).
+// One kernel serves both modes; its workgroups own 128-row windows of the rows (one 128-byte
+// line of every q_col row they touch).  Lines of q_col that two workgroups each fill in
+// part cost far more than their bytes: an earlier kernel that gave each workgroup four
+// consecutive blocks (and so split lines wherever segments start off a 32-row boundary)
+// took 980 us for the dual mode on 524288 x 2048 Zipf-routed rows, timed with the
+// write-back of the lines it left dirty, against 858 us for the window kernel.  Block
+// indices are 32-bit (ceil(M/32) + E < 2^31, checked by the caller).
 
 __device__ __forceinline__ int64_t clamp_row(int64_t r, int64_t M) { return r < 0 ? 0 : (r > M ? M : r); }
 
@@ -602,32 +601,11 @@ __device__ void group_check(const int64_t* __restrict__ off, int64_t E, int64_t 
     if (lane == 0) *status = any_bad ? 6 /* BSQ_ERR_OFFSETS */ : 0;
 }
 
-// Columnwise-only mode.  A workgroup owns a window of 128 rows and 256 columns.  The blocks
-// that overlap the window -- with segments of 32 rows or more, four or five, the first and
-// last possibly reaching outside it -- are loaded whole (a block reaching outside is loaded
-// by both neighbouring windows, mostly from cache), and only the window's rows are stored.
-// The block's scale goes out from the window that holds its first row.  Columnwise codes
-// are gathered in LDS, one 128-byte line (plus a 32-byte margin on each side) per column:
-// every lane writes its 16 codes at its rows' place -- first the lanes holding 1 to 15 rows
-// of their block, slot by slot in row order, then the lanes holding 16 -- so that where a
-// lane's codes run past its block's end (copies of the block's last row) the next block's
-// codes overwrite them; bytes that fall in the margins belong to the neighbouring windows
-// and are dropped.  The lines then leave as aligned 16-byte stores, eight lanes to a line.
-// On the 524288 x 2048 routed rows: 686 us with 128 Zipf-routed experts, 602 us with one
-// segment (the flat columnwise kernel: 633 us); the dual kernel's segmented layout without
-// the rowwise copy measured 676 and 624 us.
-//
-// Wave layout: lane l = 4 rg + c holds rows 16 (rg & 1) .. + 15 of block slot rg >> 1 and
-// columns 8 c .. 8 c + 7 of the wave's 32; a 32x1 column block is the lane pair (rg,
-// rg ^ 1), lanes 4 apart (one swizzle).  A pass covers 8 block slots; a window overlapping
-// more blocks (segments shorter than 32 rows) takes more passes.
+// A workgroup owns a window of 128 rows (one 128-byte line of every q_col row it touches)
+// and 256 columns.  Its table lists the blocks that overlap the window, in row order: with
+// segments of 32 rows or more, four or five, the first and last possibly reaching outside.
 constexpr int WIN_ROWS = 128;
-#ifndef BSQ_MXGROUP_WIN_WAVES
-#define BSQ_MXGROUP_WIN_WAVES 8
-#endif
-constexpr int WIN_WAVES = BSQ_MXGROUP_WIN_WAVES;       // 32 columns each
-constexpr int WIN_COLS = 32 * WIN_WAVES;
-constexpr int WIN_SLOTS = 8;                          // blocks per pass
+constexpr int WIN_SLOTS = 8;                          // blocks per pass of the block-slot path
 constexpr int WIN_TAB = WIN_ROWS;                     // each overlapping block holds a window row
 
 struct WindowTable {
@@ -685,118 +663,34 @@ __device__ __forceinline__ void win_join_pairs(uint32_t (&cm)[4]) {
         cm[d] = pk_absmax(cm[d], (uint32_t)__builtin_amdgcn_ds_swizzle((int)cm[d], 0x101F));  // lane ^ 4
 }
 
-__global__ __launch_bounds__(64 * WIN_WAVES)
-void mx_quant_grouped_col_window_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
-                                        const int64_t* __restrict__ off, int64_t E,
-                                        uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col, int64_t s_ld,
-                                        int64_t n_limit, int64_t col_groups, int32_t* __restrict__ status) {
-    constexpr int CP = WIN_ROWS + 64;                 // column line + margins
-    __shared__ WindowTable tab;
-    __shared__ __align__(16) uint8_t lds_c[WIN_WAVES][32][CP];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t win = blockIdx.x / col_groups;
-    const int64_t kw = (blockIdx.x - win * col_groups) * WIN_COLS;
-    const int64_t w0 = win * WIN_ROWS;
-    if (wave == 0) window_find_blocks(off, E, M, w0, n_limit, tab);
-    if (wave == 1 && status != nullptr && blockIdx.x == 0) group_check(off, E, M, s_ld, status);
-    __syncthreads();
-    const int count = tab.count;
-
-    const int rg = lane >> 2, c = lane & 3;
-    const int slot = rg >> 1, half = rg & 1;
-    const int lcol = wave * 32 + 8 * c;
-    const int64_t col = kw + lcol;
-    const bool colok = col < K;
-    const uint16_t* xc = x + (colok ? col : kw);
-    for (int p = 0; p * WIN_SLOTS < count; ++p) {
-        const int sl = WIN_SLOTS * p + slot;
-        const int blen = sl < count ? tab.len[sl] : 0;
-        const int64_t bstart = blen > 0 ? tab.start[sl] : tab.start[WIN_SLOTS * p];   // a row inside the tensor
-        const int last = (blen > 0 ? blen : 1) - 1;
-        const int64_t r0 = bstart + 16 * half;        // lane's first row
-
-        uint4 v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int ri = min(16 * half + i, last);
-            v[i] = ld_stream<MXTILE_NT_LOAD>(reinterpret_cast<const uint4*>(xc + (bstart + ri) * K));
-        }
-        const int vc = min(max(blen - 16 * half, 0), 16);      // rows of this lane inside its block
-
-        uint32_t cm[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            uint32_t unused = 0u;
-            tile_row_chunk<false>(v[i], cm, unused);
-        }
-        win_join_pairs(cm);
-        const bool own_scale = blen > 0 && half == 0 && bstart >= w0 && colok;
-        const int64_t n = tab.n[sl < WIN_TAB ? sl : 0];
-        const int lo_c = 32 + (int)(r0 - w0);            // 1 .. 175: inside the margins
-        const bool any_part = __builtin_amdgcn_ballot_w64(vc > 0 && vc < 16) != 0;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            uint4 a, b;
-            uint32_t code0, code1;
-            tile_col_codes(v, cm[d], d, a, b, code0, code1);
-            uint8_t* la = &lds_c[wave][8 * c + 2 * d][lo_c];
-            if (any_part) {                            // lanes with 1..15 rows, in slot order
-#pragma unroll
-                for (int k = 0; k < WIN_SLOTS; ++k) {
-                    if (slot == k && vc > 0 && vc < 16) {
-                        __builtin_memcpy(la, &a, 16);
-                        __builtin_memcpy(la + CP, &b, 16);
-                    }
-                }
-            }
-            if (vc == 16) {                            // then the full lanes, over any overrun
-                __builtin_memcpy(la, &a, 16);
-                __builtin_memcpy(la + CP, &b, 16);
-            }
-            if (own_scale) {
-                s_col[(col + 2 * d) * s_ld + n] = (uint8_t)code0;
-                s_col[(col + 2 * d + 1) * s_ld + n] = (uint8_t)code1;
-            }
-        }
-    }
-    // the wave's 32 column lines: 16-byte chunk q of the wave is line q / 8, part q % 8
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (kw + wave * 32 < K) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int q = lane + 64 * t, cc = q >> 3, part = q & 7;
-            const int64_t row = w0 + 16 * part;
-            uint8_t* dst = q_col + (kw + wave * 32 + cc) * M + row;
-            const uint8_t* src = &lds_c[wave][cc][32 + 16 * part];
-            if (row + 16 <= M) {
-                st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(dst), *reinterpret_cast<const uint4*>(src));
-            } else {
-                for (int j = 0; row + j < M; ++j) dst[j] = src[j];
-            }
-        }
-    }
-}
-
-// Dual mode with line ownership.  Same 128-row windows, with the flat tile's layout (lane
+// The window kernel.  Each wave holds the window's rows in the flat tile's layout (lane
 // 8g + c holds window rows 16g .. 16g+15, columns 8c .. 8c+7 of its wave's 64), so every
-// lane works on rows of the window and the rowwise copy costs what it costs in the flat
-// kernel.  The 32x1 block maxima are segmented: each lane folds its rows into at most two
-// partial maxima (its rows meet at most two blocks when every block holds 16 rows or
-// more), the lanes with rows of the blocks that reach outside the window fold those rows
-// too, and the partial maxima meet in an LDS table of the window's blocks (ds_max per
-// column; each wave has its own table for its 64 columns, so only a wave barrier waits
-// for it).  Each row is then encoded with its own block's scale: the codes of a lane's
-// rows before and after its block boundary come from two converts and a byte select (one
-// convert when no lane of the wave has a boundary inside its rows).  The columnwise codes
-// leave as one 16-byte store per lane and column, eight lanes filling a q_col line.
-// Windows with more than DW_BLOCKS blocks, or with a block shorter than 16 rows, take the
-// block-slot path of the columnwise kernel instead (with the rowwise copy added).
-// Launched for three workgroups per compute unit (168 VGPRs; the compiler spills a few
-// 64-bit values, 32 bytes a lane, outside the per-row work): on the Zipf-routed rows
-// 892 us against 1010 us at two workgroups.
+// lane works on rows of the window and the rowwise copy (ROWWISE) costs what it costs in
+// the flat kernel.  The 32x1 block maxima are segmented: each lane folds its rows into at
+// most two partial maxima (the fast path requires that no lane's rows meet three blocks,
+// which holds whenever every block has 16 rows or more), the rows of the blocks that reach
+// outside the window are folded too (one list of four rows a lane when both edge blocks
+// lie in one segment), and the partial maxima meet in an LDS table of the window's blocks
+// (ds_max per column; each wave has its own table for its 64 columns, so only a wave
+// barrier waits for it).  Each row is then encoded with its own block's scale: the codes
+// of a lane's rows before and after its block boundary come from two converts and a byte
+// select (one convert when no lane of the wave has a boundary inside its rows).  The
+// columnwise codes leave as one 16-byte store per lane and column, eight lanes filling a
+// q_col line.  Other windows (more than DW_BLOCKS blocks, or a lane meeting three) take a
+// block-slot path: lane 4 rg + c holds rows 16 (rg & 1) .. + 15 of block slot rg >> 1, 32
+// columns at a time, a block whose rows reach outside the window is loaded whole and only
+// the window's rows are stored.  A FULL variant (M % 128 == 0, K % 256 == 0) drops the
+// bounds masks.
+// Launched for three workgroups per compute unit (168 VGPRs for the dual mode, where the
+// compiler spills a few 64-bit values, 28 bytes a lane, outside the per-row work; 152 for
+// the columnwise mode).  On the 524288 x 2048 Zipf-routed rows, on one box: dual mode 858
+// us (892 before the FULL variant and the shared edge list, 1010 at two workgroups per
+// compute unit); issuing the window loads before the block table is built, so that the
+// table's lookups overlap them, measured 10 us slower.  Columnwise mode 651 us against 682
+// for a block-slot kernel of eight waves (half its lanes idle on aligned windows; it wins
+// only there, 603 against 620 us).
 constexpr int DW_BLOCKS = 8;
+
 
 // Bytes k of a 4-row group whose row 4u + k lies before the boundary b (t = b - 4u).
 __device__ __forceinline__ uint32_t split_mask(int t) {
@@ -832,24 +726,23 @@ __device__ __forceinline__ void tile_col_codes_split(const uint4 (&v)[16], int d
 // The 8 column maxima of a lane (packed pairs) into row j of the block table.
 __device__ __forceinline__ void dw_put(uint32_t (*bmax)[TILE_COLS], int j, int lcol, const uint32_t (&cm)[4]) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t m = (e & 1) ? (cm[e >> 1] >> 16) : (cm[e >> 1] & 0xFFFFu);
-        if (m != 0u) atomicMax(&bmax[j][lcol + e], m);
-    }
+    for (int e = 0; e < 8; ++e)
+        atomicMax(&bmax[j][lcol + e], (e & 1) ? (cm[e >> 1] >> 16) : (cm[e >> 1] & 0xFFFFu));
 }
 
 typedef uint32_t u32x4u_t __attribute__((ext_vector_type(4), aligned(1)));
 
+template <bool FULL, bool ROWWISE>
 __global__ __launch_bounds__(256, 3)
-void mx_quant_grouped_dual_window_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+void mx_quant_grouped_window_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                          const int64_t* __restrict__ off, int64_t E,
                                          uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
                                          uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col, int64_t s_ld,
                                          int64_t n_limit, int64_t col_groups, int32_t* __restrict__ status) {
     using G = TileGeom<1, 4>;                          // 128 rows x 256 columns, 4 waves
     __shared__ WindowTable tab;
-    __shared__ __align__(16) uint8_t lds_srow[G::ROWS][G::SROW_B];
-    __shared__ __align__(16) uint8_t lds_q[G::ROWS][G::QPITCH];
+    __shared__ __align__(16) uint8_t lds_srow[ROWWISE ? G::ROWS : 1][G::SROW_B];
+    __shared__ __align__(16) uint8_t lds_q[ROWWISE ? G::ROWS : 1][G::QPITCH];
     __shared__ uint32_t bmax_w[4][DW_BLOCKS][TILE_COLS];       // per wave: its 64 columns
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t win = blockIdx.x / col_groups;
@@ -859,28 +752,55 @@ void mx_quant_grouped_dual_window_kernel(const uint16_t* __restrict__ x, int64_t
     if (wave == 1 && status != nullptr && blockIdx.x == 0) group_check(off, E, M, s_ld, status);
     __syncthreads();
     const int count = tab.count;
+    // fast path: every lane's 16 rows meet at most two blocks, i.e. no block that starts off a
+    // lane's first row is followed by another start among the same lane's rows (uniform)
     bool fast = count >= 1 && count <= DW_BLOCKS;
-    for (int j = 0; j < count && fast; ++j) fast = tab.len[j] >= 16;   // uniform
+    for (int j = 1; j + 1 < count && fast; ++j) {
+        const int64_t a = tab.start[j] - w0, b = tab.start[j + 1] - w0;   // 0 < a < b < WIN_ROWS
+        fast = (a & 15) == 0 || (a >> 4) != (b >> 4);
+    }
 
     if (fast) {
         const int g = lane >> 3, c = lane & 7;
         const int lcol = wave * TILE_COLS + 8 * c;
         const int64_t col = kw + lcol;
-        const bool colok = col < K;
+        const bool colok = FULL || col < K;
         const uint16_t* xc = x + (colok ? col : kw);
         uint32_t (*bmax)[TILE_COLS] = bmax_w[wave];
         const int wcol = 8 * c;                        // the lane's first column in the wave
 #pragma unroll
         for (int i = 0; i < DW_BLOCKS; ++i) bmax[i][lane] = 0u;
         const int64_t r0 = w0 + 16 * g;                // the lane's first row
-        const int hi = (int)max<int64_t>(min<int64_t>(M - r0, 16), 0);   // its rows inside the tensor
-        // rows of the blocks that reach outside the window: 4 before and 4 after it a lane,
-        // folded before the window rows are loaded (fewer registers live at once)
+        const int hi = FULL ? 16 : (int)max<int64_t>(min<int64_t>(M - r0, 16), 0);   // its rows in the tensor
+        // rows of the blocks that reach outside the window, folded before the window rows are
+        // loaded (fewer registers live at once): nh rows before it and nt after it, 1..31 each.
+        // Inside one segment nh + nt = 32, and the two lists share one set of four loads a lane;
+        // otherwise each list takes four.
         const int64_t hs = tab.start[0];               // head block, if it starts before w0
         const int64_t te = tab.start[count - 1] + tab.len[count - 1];   // tail block's end
         const bool head = hs < w0, tail = te > w1;     // uniform
+        const int nh = head ? (int)(w0 - hs) : 0, nt = tail ? (int)(te - w1) : 0;
         uint32_t ch[4] = {0u, 0u, 0u, 0u}, ct[4] = {0u, 0u, 0u, 0u};
-        if (head || tail) {
+        if ((head || tail) && nh + nt <= 32) {
+            uint4 e[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int idx = 4 * g + t;             // entry of the list [hs, w0) ++ [w1, te)
+                const int64_t r = idx < nh ? hs + idx : idx < nh + nt ? w1 + (idx - nh) : w0;
+                e[t] = ld_stream<MXTILE_NT_LOAD>(reinterpret_cast<const uint4*>(xc + r * K));
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int idx = 4 * g + t;
+                const bool vh = idx < nh, vt = idx >= nh && idx < nh + nt;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t m = dword_of(e[t], d) & 0x7FFF7FFFu;
+                    ch[d] = pk_absmax(ch[d], vh ? m : 0u);
+                    ct[d] = pk_absmax(ct[d], vt ? m : 0u);
+                }
+            }
+        } else if (head || tail) {
             uint4 eh[4], et[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -904,7 +824,7 @@ void mx_quant_grouped_dual_window_kernel(const uint16_t* __restrict__ x, int64_t
             v[i] = ld_stream<MXTILE_NT_LOAD>(reinterpret_cast<const uint4*>(xc + (i < hi ? r0 + i : w0) * K));
         // rowwise codes, staged in LDS
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 16 && ROWWISE; ++i) {
             uint32_t code = 0u, unused[4] = {0u, 0u, 0u, 0u};
             const uint2 out = tile_row_chunk<true>(v[i], unused, code);
             if (i < hi) {
@@ -1010,8 +930,8 @@ void mx_quant_grouped_dual_window_kernel(const uint16_t* __restrict__ x, int64_t
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     uint32_t code = 0u;
-                    const uint2 out = tile_row_chunk<true>(v[i], cm, code);
-                    if (i >= ilo && i < ihi) {
+                    const uint2 out = tile_row_chunk<ROWWISE>(v[i], cm, code);
+                    if (ROWWISE && i >= ilo && i < ihi) {
                         const int wr = (int)(r0 - w0) + i;             // 0 <= wr < WIN_ROWS
                         *reinterpret_cast<uint2*>(&lds_q[wr][lcol]) = out;
                         lds_srow[wr][lcol >> 5] = (uint8_t)code;
@@ -1050,13 +970,14 @@ void mx_quant_grouped_dual_window_kernel(const uint16_t* __restrict__ x, int64_t
             }
         }
     }
+    if (!ROWWISE) return;
     __syncthreads();
     // rowwise codes and scales of the window's rows
-    const int L = (int)min<int64_t>(WIN_ROWS, M - w0);
+    const int L = FULL ? WIN_ROWS : (int)min<int64_t>(WIN_ROWS, M - w0);
     constexpr int CHUNKS = G::COLS / 16;
     for (int idx = threadIdx.x; idx < L * CHUNKS; idx += G::THREADS) {
         const int r = idx / CHUNKS, c16 = idx % CHUNKS;
-        if (kw + 16 * c16 < K) {
+        if (FULL || kw + 16 * c16 < K) {
             const uint4 val = *reinterpret_cast<const uint4*>(&lds_q[r][16 * c16]);
             st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(q_row + (w0 + r) * K + kw + 16 * c16), val);
         }
@@ -1088,19 +1009,14 @@ hipError_t launch_mx_quant_grouped(const void* x, int64_t M, int64_t K, int mode
             hipLaunchKernelGGL(mx_group_check_kernel, dim3(1), dim3(64), 0, stream, off, E, M, s_ld, status);
         return hipGetLastError();
     }
-    if (mode == 3) {
-        const int64_t col_groups = (K + 255) / 256;
-        const int64_t grid = (M + WIN_ROWS - 1) / WIN_ROWS * col_groups;
-        hipLaunchKernelGGL(mx_quant_grouped_dual_window_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                           (const uint16_t*)x, M, K, off, E, (uint8_t*)q_row, (uint8_t*)s_row,
-                           (uint8_t*)q_col, (uint8_t*)s_col, s_ld, n_limit, col_groups, status);
-    } else {
-        const int64_t col_groups = (K + WIN_COLS - 1) / WIN_COLS;
-        const int64_t grid = (M + WIN_ROWS - 1) / WIN_ROWS * col_groups;
-        hipLaunchKernelGGL(mx_quant_grouped_col_window_kernel, dim3((unsigned)grid), dim3(64 * WIN_WAVES), 0, stream,
-                           (const uint16_t*)x, M, K, off, E, (uint8_t*)q_col, (uint8_t*)s_col, s_ld, n_limit,
-                           col_groups, status);
-    }
+    const int64_t col_groups = (K + 255) / 256;
+    const int64_t grid = (M + WIN_ROWS - 1) / WIN_ROWS * col_groups;
+    const bool full = M % WIN_ROWS == 0 && K % 256 == 0;   // no ragged window or column group
+    const auto kernel = mode == 3 ? (full ? mx_quant_grouped_window_kernel<true, true> : mx_quant_grouped_window_kernel<false, true>)
+                                  : (full ? mx_quant_grouped_window_kernel<true, false> : mx_quant_grouped_window_kernel<false, false>);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const uint16_t*)x, M, K, off, E, (uint8_t*)q_row, (uint8_t*)s_row,
+                       (uint8_t*)q_col, (uint8_t*)s_col, s_ld, n_limit, col_groups, status);
     return hipGetLastError();
 }
 

@@ -49,6 +49,14 @@ def _cases():
     yield "many", 5000, 512, _counts_offsets(np.diff(np.sort(np.concatenate(
         [[0, 5000], rng.integers(0, 5000, size=36)]))).tolist())
     yield "aligned_16", 1024, 256, _counts_offsets([16, 48, 112, 0, 336, 512])
+    # whole 128-row windows and 256-column groups, segments off the 32-row grid whose blocks
+    # all hold 16 rows or more: blocks reach across windows on both sides, from one segment
+    # or from two
+    counts = rng.integers(40, 400, size=40)
+    counts = np.where((counts % 32 > 0) & (counts % 32 < 16), counts + 16, counts)
+    counts = counts[np.cumsum(counts) <= 8192 - 48].tolist()
+    counts.append(8192 - sum(counts))
+    yield "whole_windows_off_grid", 8192, 512, _counts_offsets(counts)
 
 
 CASES = list(_cases())
