@@ -62,12 +62,8 @@ def _cases():
 CASES = list(_cases())
 
 
-@pytest.mark.parametrize("mode", [bsq.MX_COLWISE, bsq.MX_BOTH])
-@pytest.mark.parametrize("name,M,K,off", CASES, ids=[c[0] for c in CASES])
-def test_grouped_matches_oracle(name, M, K, off, mode):
-    assert off[-1] == M
-    log("mx grouped %s %dx%d E=%d mode %d" % (name, M, K, len(off) - 1, mode))
-    x = mixed_bf16(np.random.default_rng(M * 13 + K + mode), M, K)
+def _check_grouped(x, off, mode):
+    M, K = x.shape
     nb = int(oracle.mx_group_blocks(off).sum())
     s_ld = nb + 3                                              # room past the last block
     qr, sr, qc, sc, status = _grouped_gpu(x, off, mode, s_ld)
@@ -91,9 +87,53 @@ def test_grouped_matches_oracle(name, M, K, off, mode):
 
 
 @pytest.mark.parametrize("mode", [bsq.MX_COLWISE, bsq.MX_BOTH])
+@pytest.mark.parametrize("name,M,K,off", CASES, ids=[c[0] for c in CASES])
+def test_grouped_matches_oracle(name, M, K, off, mode):
+    assert off[-1] == M
+    log("mx grouped %s %dx%d E=%d mode %d" % (name, M, K, len(off) - 1, mode))
+    x = mixed_bf16(np.random.default_rng(M * 13 + K + mode), M, K)
+    _check_grouped(x, off, mode)
+
+
+def _random_counts(rng, M):
+    """Segment lengths mixing the cases the kernel tells apart: empty experts, 1-15 rows,
+    16-31 rows, a few rows either side of a multiple of 32, and long segments."""
+    counts, total = [], 0
+    while total < M:
+        kind = int(rng.integers(0, 5))
+        if kind == 0:
+            c = 0
+        elif kind == 1:
+            c = int(rng.integers(1, 16))
+        elif kind == 2:
+            c = int(rng.integers(16, 32))
+        elif kind == 3:
+            c = int(32 * rng.integers(1, 5) + rng.integers(-2, 3))
+        else:
+            c = int(rng.integers(33, 300))
+        c = min(c, M - total)
+        counts.append(c)
+        total += c
+    return counts
+
+
+@pytest.mark.parametrize("mode", [bsq.MX_COLWISE, bsq.MX_BOTH])
+@pytest.mark.parametrize("seed", range(8))
+def test_grouped_random_segments(seed, mode):
+    """Random segment mixes over whole and ragged windows and column groups."""
+    rng = np.random.default_rng(1000 + seed)
+    M = int(rng.choice([640, 1024, 1500, 2048, 3001]))
+    K = int(rng.choice([32, 160, 256, 512]))
+    off = _counts_offsets(_random_counts(rng, M))
+    log("mx grouped random seed %d %dx%d E=%d mode %d" % (seed, M, K, len(off) - 1, mode))
+    x = mixed_bf16(rng, M, K)
+    _check_grouped(x, off, mode)
+
+
+@pytest.mark.parametrize("mode", [bsq.MX_COLWISE, bsq.MX_BOTH])
 def test_grouped_more_than_2_pow_23_rows(mode):
     """q_col past 2^31 bytes from its base with 1000 segments of random length (most not
-    multiples of 32): 64-bit addressing in both grouped kernels."""
+    multiples of 32): 64-bit addressing in both modes of the grouped kernel."""
     M, K = (1 << 23) + 48, 32
     log("mx grouped large %dx%d mode %d" % (M, K, mode))
     rng = np.random.default_rng(29)
