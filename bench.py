@@ -377,19 +377,16 @@ def all_configs(torch, bsq, workloads, dev, reps=21):
     torch.cuda.synchronize()
 
 
-def cpu_baseline(a_np, w_np, tok, frac, reps):
-    """The CPU oracle (as it stands, OpenMP over rows) on 1/frac of the step's rows, reps
-    times over: the first M/frac rows of A (both copies), the first rows of W, the first
+def _oracle_step_sample(oracle, a_np, w_np, tok, frac, reps):
+    """Time the CPU oracle (as it stands, OpenMP over rows) on 1/frac of the step's rows,
+    reps times over: the first M/frac rows of A (both copies), the first rows of W, the first
     R/frac routed rows, and the dequantization of all of those outputs."""
-    import oracle
-
     MA = (a_np.shape[0] // frac) // 32 * 32
     MW = max(32, (w_np.shape[0] // frac) // 32 * 32)
     RX = tok.size // frac
     a_s = np.ascontiguousarray(a_np[:MA])
     w_s = np.ascontiguousarray(w_np[:MW])
     x_s = a_np[tok[:RX]]
-    oracle.lib()
     t0 = time.perf_counter()
     for _ in range(reps):
         for m in (a_s, w_s):
@@ -403,10 +400,28 @@ def cpu_baseline(a_np, w_np, tok, frac, reps):
     KA, KW, KX = a_s.shape[1], w_s.shape[1], x_s.shape[1]
     b = reps * (mx_both_bytes(MA, KA) + mx_both_bytes(MW, KW) + 2 * nv_bytes(RX, KX)
                 + 2 * mx_dq_bytes(MA, KA) + 2 * mx_dq_bytes(MW, KW))
-    return {"value": round(b / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.max_threads(),
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "%d x 1/%d of the step: A[:%d] and W[:%d] MXFP8 dual + dequant of both copies, "
-                      "%d routed rows NVFP4 + dequant" % (reps, frac, MA, MW, RX)}
+    sample = ("%d x 1/%d of the step: A[:%d] and W[:%d] MXFP8 dual + dequant of both copies, "
+              "%d routed rows NVFP4 + dequant" % (reps, frac, MA, MW, RX))
+    return round(b / dt / 1e9, 3), round(dt, 2), sample
+
+
+def cpu_baseline(a_np, w_np, tok, frac, reps):
+    """The CPU oracle on a bounded sample of the step, with all host threads, and once more
+    on a 32x smaller sample with one thread."""
+    import oracle
+
+    oracle.lib()
+    cores = oracle.max_threads()
+    gbs, secs, sample = _oracle_step_sample(oracle, a_np, w_np, tok, frac, reps)
+    oracle.set_threads(1)
+    try:
+        gbs1, secs1, sample1 = _oracle_step_sample(oracle, a_np, w_np, tok, frac * 32, 1)
+    finally:
+        oracle.set_threads(cores)
+    return {"value": gbs, "unit": "GB/s", "cores": cores, "kind": "oracle", "seconds": secs,
+            "sample": sample,
+            "single_thread": {"value": gbs1, "unit": "GB/s", "cores": 1, "seconds": secs1,
+                              "sample": sample1}}
 
 
 if __name__ == "__main__":

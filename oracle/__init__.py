@@ -102,6 +102,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_rne_bf16_f32_range.argtypes = [ctypes.c_uint32, I64, P]
         L.oracle_max_threads.restype = ctypes.c_int
         L.oracle_max_threads.argtypes = []
+        L.oracle_set_threads.restype = None
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
 
@@ -383,3 +385,8 @@ def rne_bf16_f32_range(start: int, n: int) -> np.ndarray:
 
 def max_threads() -> int:
     return lib().oracle_max_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (for timing; results do not depend on it)."""
+    lib().oracle_set_threads(int(n))

@@ -534,3 +534,13 @@ int oracle_max_threads(void) {
     return 1;
 #endif
 }
+
+/* Threads of the parallel loops above (timing only; the results do not depend on it). */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}
