@@ -87,7 +87,68 @@ def parse():
     p.add_argument("--profile-pass", action="store_true",
                    help="short run for hardware-counter passes: one 1 GiB device copy (the "
                         "counter calibration kernel), then the steps")
+    p.add_argument("--profile-op", choices=sorted(PROFILE_OPS),
+                   help="counter pass of one extended op: one 1 GiB device copy, then the op "
+                        "twice on random inputs of the benchmark's shapes")
     return p.parse_args()
+
+
+PROFILE_OPS = ("per_group_quant", "per_group_dequant", "tile16_quant", "tile16_dequant",
+               "scatter", "grouped_dual", "grouped_colwise")
+
+
+def profile_op(torch, bsq, workloads, dev, op):
+    """One extended op, twice, after a 1 GiB copy, for rocprofv3 counter passes: the
+    per-expert-scale and 16x16-tile NVFP4 export of the stacked gate_up weights (196608 x
+    2048, 128 groups), quantize-then-scatter of 65536 tokens to 8 routed rows each, and
+    grouped MXFP8 of 524288 x 2048 rows over 128 experts with Zipf(1.1) top-8 routing."""
+    torch.manual_seed(0)
+    u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+    src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    if op.startswith(("per_group", "tile16")):
+        M, K, rows = 196608, 2048, 1536
+        w = (torch.randn(M, K, device=dev) * 0.02).to(bf)
+        off = torch.arange(0, M + 1, rows, dtype=torch.int64, device=dev)
+        q, y = torch.empty(M, K // 2, dtype=u8, device=dev), torch.empty(M, K, dtype=bf, device=dev)
+        sb, sb2 = torch.empty(M, K // 16, dtype=u8, device=dev), torch.empty(M // 16, K // 16, dtype=u8, device=dev)
+        sg, st = torch.empty(M // rows, dtype=f32, device=dev), torch.zeros(1, dtype=torch.int32, device=dev)
+        if op == "per_group_dequant":
+            bsq.nv_quantize_nvfp4_per_group(w, off, q, sb, sg, st)
+        if op == "tile16_dequant":
+            bsq.nv_quantize_nvfp4_2d(w, off, q, sb2, sg, st)
+        fn = {"per_group_quant": lambda: bsq.nv_quantize_nvfp4_per_group(w, off, q, sb, sg, st),
+              "per_group_dequant": lambda: bsq.nv_dequantize_per_group(q, sb, sg, off, y),
+              "tile16_quant": lambda: bsq.nv_quantize_nvfp4_2d(w, off, q, sb2, sg, st),
+              "tile16_dequant": lambda: bsq.nv_dequantize_2d(q, sb2, sg, off, y)}[op]
+    elif op == "scatter":
+        T, K, k = 65536, 2048, 8
+        h = (torch.randn(T, K, device=dev) * 2).to(bf)
+        rows_of = torch.randperm(T * k, device=dev).reshape(T, k)
+        N = T * k
+        out = (torch.empty(N, K // 2, dtype=u8, device=dev), torch.empty(N, K // 16, dtype=u8, device=dev),
+               torch.empty(N, dtype=f32, device=dev), torch.zeros(1, dtype=torch.int32, device=dev))
+        fn = lambda: bsq.nv_quantize_nvfp4_per_token_scatter(h, rows_of, N, *out)
+    else:
+        M, K = 524288, 2048
+        x = (torch.randn(M, K, device=dev) * 2).to(bf)
+        _, off_np = workloads.zipf_routing(np.random.default_rng(4), 65536, 128, 8)
+        off = torch.from_numpy(off_np).to(dev)
+        s_ld = bsq.mx_group_scale_entries(M, off.numel() - 1)
+        out = (torch.empty(M, K, dtype=u8, device=dev), torch.empty(M, K // 32, dtype=u8, device=dev),
+               torch.empty(K, M, dtype=u8, device=dev), torch.empty(K, s_ld, dtype=u8, device=dev),
+               torch.zeros(1, dtype=torch.int32, device=dev))
+        if op == "grouped_dual":
+            fn = lambda: bsq.mx_quantize_mxfp8_grouped(x, off, "both", s_ld, *out)
+        else:
+            fn = lambda: bsq.mx_quantize_mxfp8_grouped(x, off, "colwise", s_ld, None, None, *out[2:])
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_op": op}), flush=True)
 
 
 def main():
@@ -111,6 +172,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.all_configs:
         return all_configs(torch, bsq, workloads, dev)
+    if args.profile_op:
+        return profile_op(torch, bsq, workloads, dev, args.profile_op)
     t_gen = time.time()
     cfg = workloads.config5()
     a_np, w_np, tok, off = cfg["a"], cfg["w"], cfg["token_idx"], cfg["offsets"]

@@ -57,6 +57,8 @@ def _cases():
     counts = counts[np.cumsum(counts) <= 8192 - 48].tolist()
     counts.append(8192 - sum(counts))
     yield "whole_windows_off_grid", 8192, 512, _counts_offsets(counts)
+    # the same segments over eight 256-column groups
+    yield "whole_windows_off_grid_wide", 8192, 2048, _counts_offsets(counts)
 
 
 CASES = list(_cases())
