@@ -52,6 +52,14 @@
  * build uses -fno-fast-math -ffp-contract=off and the check below rules out
  * excess precision, so each float operation is one IEEE binary32 operation,
  * rounded to nearest-even, with gradual underflow.
+ *
+ * Parity unpinned: the readings listed above (the all-zero block code, the sign of zero
+ * codes, the nibble order, the direction of the FP32 scale and the binary32 operation
+ * order of the NVFP4 scale steps), and the layouts of the grouped, per-group, 16x16-tile
+ * and scatter calls, are fixed by this implementation, not by the pages, which print no
+ * worked example.  They are checked against a second implementation of the same readings
+ * (the exact-rational verifier), against hand-worked fixtures, and against the flat calls
+ * and properties they reduce to; nothing on the pages can confirm the choices themselves.
  */
 #include <float.h>
 #include <math.h>
