@@ -35,3 +35,20 @@ def test_traffic_record_names_its_sources_and_scales():
     for p in rec["kernel_sources"]:
         assert os.path.exists(os.path.join(ROOT, p))
     assert abs(rec["fetch_size_scale"] - 2.0) < 0.01 and abs(rec["write_size_scale"] - 1.0) < 0.01
+
+
+def test_cpu_baseline_reports_the_oracle_with_all_threads_and_with_one():
+    import numpy as np
+    import oracle
+    import workloads
+    rng = np.random.default_rng(5)
+    a = workloads.bf16_bits_from_f32(rng.standard_normal((2048, 256)).astype(np.float32))
+    w = workloads.bf16_bits_from_f32(rng.standard_normal((64, 512)).astype(np.float32))
+    tok = rng.integers(0, 2048, size=4096)
+    threads = oracle.max_threads()
+    r = bench.cpu_baseline(a, w, tok, 1, 1)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["value"] > 0
+    assert r["cores"] == threads and "sample" in r
+    st = r["single_thread"]
+    assert st["cores"] == 1 and st["value"] > 0 and "1/32" in st["sample"]
+    assert oracle.max_threads() == threads                    # restored afterwards
