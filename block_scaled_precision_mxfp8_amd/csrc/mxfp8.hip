@@ -12,8 +12,9 @@
 //
 // The work is pure streaming (about 3-4 bytes of HBM traffic per element and a few
 // integer/FP32 operations), so the kernels are written for HBM bandwidth: 16-byte loads
-// and stores that cover whole cache lines per instruction, block maxima reduced inside a
-// quad of lanes with DPP, and no LDS traffic on the element data.
+// and stores that cover whole cache lines per instruction, and block maxima reduced inside
+// a quad or pair of lanes with DPP.  LDS carries no element data in, only codes and scale
+// bytes on their way out, where staging lets whole lines leave in one store.
 #include "bsq_device.h"
 
 namespace bsq {

@@ -1,5 +1,6 @@
-// nvfp4.hip -- per-token NVFP4 quantization (flat and grouped by expert) and NVFP4
-// dequantization to BF16 for gfx950.
+// nvfp4.hip -- per-token NVFP4 quantization (flat, grouped by expert, and quantize-then-
+// scatter of routed rows), NVFP4 with one FP32 scale per row group (per tensor or expert)
+// and with 16x16 weight tiles, and NVFP4 dequantization to BF16, for gfx950.
 //
 // Page "Towards Blackwell-native 8-bit and 4-bit RL":
 //  * section "Format background": E2M1 values, one E4M3 scale per 16 values rounded to
@@ -12,9 +13,10 @@
 //  * section "High-precision and dequantized backward": BF16 dequantized operands.
 //
 // The per-token scale needs the whole row before any element can be encoded.  A wave
-// owns a row and keeps it in registers (16-byte loads, 8 BF16 per lane per slot), so the
-// row is read from HBM exactly once: row maximum by a wave reduction, then each 1x16
-// block (a lane pair) is scaled and encoded from registers.
+// owns a row (two rows when they are 768 elements or shorter) and keeps it in registers
+// (16-byte loads, 8 BF16 per lane per slot), so the row is read from HBM exactly once:
+// row maximum by a wave reduction, then each 1x16 block (a lane pair) is scaled and
+// encoded from registers.
 #include <float.h>
 
 #include "bsq_device.h"
