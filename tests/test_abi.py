@@ -268,3 +268,54 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(bsq, "LIB_PATH", str(tmp_path / "libbsq.so"))
     with pytest.raises(ImportError, match="not built"):
         bsq.lib()
+
+
+# Random argument sets with exactly one defect each (a property test of the host validation):
+# the call must return that defect's status before any launch.
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+_MX_REQUIRED = {1: ("qr", "sr"), 2: ("qc", "sc"), 3: ("qr", "sr", "qc", "sc")}
+
+
+@st.composite
+def _mx_defective_call(draw):
+    mode = draw(st.sampled_from([1, 2, 3]))
+    M = 32 * draw(st.integers(1, 64))
+    K = 32 * draw(st.integers(1, 64))
+    args = dict(x=A, M=M, K=K, mode=mode, qr=B, sr=C, qc=D, sc=E_)
+    defect = draw(st.sampled_from(["mode", "k_mod", "m_mod", "neg", "null", "align", "alias"]))
+    if defect == "mode":
+        args["mode"] = draw(st.sampled_from([0, 4, 5, -1, 7]))
+        want = bsq.BSQ_ERR_MODE
+    elif defect == "k_mod":
+        args["K"] = K + draw(st.integers(1, 31))
+        want = bsq.BSQ_ERR_SHAPE
+    elif defect == "m_mod":
+        args["mode"] = draw(st.sampled_from([2, 3]))
+        args["M"] = M + draw(st.integers(1, 31))
+        want = bsq.BSQ_ERR_SHAPE
+    elif defect == "neg":
+        key = draw(st.sampled_from(["M", "K"]))
+        args[key] = -draw(st.integers(1, 1 << 20))
+        want = bsq.BSQ_ERR_SHAPE
+    elif defect == "null":
+        key = draw(st.sampled_from(("x",) + _MX_REQUIRED[mode]))
+        args[key] = None
+        want = bsq.BSQ_ERR_NULL
+    elif defect == "align":
+        key = draw(st.sampled_from(("x",) + _MX_REQUIRED[mode]))
+        args[key] += draw(st.integers(1, 15))
+        want = bsq.BSQ_ERR_ALIGN
+    else:                                              # an output inside the input or another output
+        key = draw(st.sampled_from(_MX_REQUIRED[mode]))
+        other = draw(st.sampled_from([k for k in ("x",) + _MX_REQUIRED[mode] if k != key]))
+        args[key] = args[other] + 16 * draw(st.integers(0, 1))   # every buffer here is >= 32 bytes
+        want = bsq.BSQ_ERR_ALIAS
+    return args, want
+
+
+@settings(max_examples=400, deadline=None)
+@given(_mx_defective_call())
+def test_mx_quant_rejects_every_single_defect(L, call):
+    args, want = call
+    assert mxq(L, **args) == want, args
