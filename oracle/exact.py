@@ -268,35 +268,148 @@ def _f32(sign: int, a: Fraction):
     return rn_binary32(sign, a)
 
 
+def nv_block(blk, s):
+    """One NVFP4 block -- a list of (sign, magnitude) pairs, the 16 values of a 1x16 block or
+    the 256 of a 16x16 tile -- under the FP32 scale s (an exact binary32 magnitude) ->
+    (E4M3 scale code, E2M1 codes in the block's order)."""
+    amax_b = max(v for _, v in blk)
+    if s == 0:
+        sb = 0
+    else:
+        _, p = _f32(0, 6 * s)                            # fl(6 * s)
+        _, t = _f32(0, amax_b / p)                       # fl(amax_b / p)
+        sb = enc_e4m3(0, t)
+    _, d = _f32(0, e4m3_value(sb) * s)                   # fl(DEC(sb) * s)
+    if d == 0:
+        f = Fraction(0)
+    else:
+        _, f = _f32(0, 1 / d)                            # fl(1 / D)
+        if f == INF:
+            f = (2 - _pow2(-23)) * _pow2(127)            # FLT_MAX
+    codes = []
+    for sg, v in blk:
+        _, y = _f32(sg, v * f)                           # fl(x * f)
+        codes.append(enc_e2m1(sg, y))
+    return sb, codes
+
+
+def _pack(codes: Sequence[int]) -> List[int]:
+    return [codes[i] | (codes[i + 1] << 4) for i in range(0, len(codes), 2)]
+
+
+def nv_row_under(bits: Sequence[int], s):
+    """One row of BF16 patterns (len % 16 == 0) encoded in 1x16 blocks under the given FP32
+    scale s (exact binary32 magnitude) -> (packed q bytes, sb codes)."""
+    vals = [bf16_value(b) for b in bits]
+    sbs, codes = [], []
+    for b in range(0, len(vals), 16):
+        sb, c = nv_block(vals[b:b + 16], s)
+        sbs.append(sb)
+        codes.extend(c)
+    return _pack(codes), sbs
+
+
 def nv_row(bits: Sequence[int]):
     """One row of BF16 patterns (len % 16 == 0) -> (packed q bytes, sb codes, s_t magnitude
     as an exact binary32 value)."""
-    vals = [bf16_value(b) for b in bits]
-    amax_t = max(v for _, v in vals)
+    amax_t = max(bf16_value(b)[1] for b in bits)
     _, s_t = _f32(0, amax_t / 2688)                     # fl(amax_t / 2688)
-    sbs, codes = [], []
-    for b in range(0, len(vals), 16):
-        blk = vals[b:b + 16]
-        amax_b = max(v for _, v in blk)
-        if s_t == 0:
-            sb = 0
-        else:
-            _, p = _f32(0, 6 * s_t)                      # fl(6 * s_t)
-            _, t = _f32(0, amax_b / p)                   # fl(amax_b / p)
-            sb = enc_e4m3(0, t)
-        sbs.append(sb)
-        _, d = _f32(0, e4m3_value(sb) * s_t)             # fl(DEC(sb) * s_t)
-        if d == 0:
-            f = Fraction(0)
-        else:
-            _, f = _f32(0, 1 / d)                        # fl(1 / D)
-            if f == INF:
-                f = (2 - _pow2(-23)) * _pow2(127)        # FLT_MAX
-        for s, v in blk:
-            _, y = _f32(s, v * f)                        # fl(x * f)
-            codes.append(enc_e2m1(s, y))
-    packed = [codes[i] | (codes[i + 1] << 4) for i in range(0, len(codes), 2)]
+    packed, sbs = nv_row_under(bits, s_t)
     return packed, sbs, s_t
+
+
+# ---------------------------------------------------------------------------------------
+# NVFP4 with one FP32 scale per row group, and with 16x16 weight tiles
+# ---------------------------------------------------------------------------------------
+#
+# Section "Format background": the scope of the coarse FP32 scale (a tensor, a batch, a
+# token) is a recipe choice; section "Per-token activation scaling": gate and up are
+# quantized together so that both get one scale.  Page "NVIDIA verified the 4-bit NVFP4
+# format on a Mamba-Transformer (12B) at 10 trillion tokens": two-dimensional block scaling
+# of the weights.  Reading (the same as the C oracle's, restated here): a group of rows
+# [o_g, o_{g+1}) gets s_g = fl(amax_g / 2688) over all its values (0 for an empty group);
+# its blocks -- 1x16 along a row, or 16x16 tiles -- are encoded with the per-token steps
+# under s_g.  These functions walk group by group, tile by tile, and index every output
+# from that walk; the C oracle walks rows and looks each row's group up.
+
+def group_scale(x: Sequence[Sequence[int]], lo: int, hi: int):
+    """s_g = fl(amax over rows lo..hi-1 / 2688) as an exact binary32 magnitude."""
+    amax = Fraction(0)
+    for r in range(lo, hi):
+        for b in x[r]:
+            amax = max(amax, bf16_value(b)[1])
+    return _f32(0, amax / 2688)[1]
+
+
+def nv_quantize_per_group(x: Sequence[Sequence[int]], offsets: Sequence[int]):
+    """Rows of BF16 patterns and group offsets -> (packed q rows, sb rows, [s_g])."""
+    R = len(x)
+    q, sb = [None] * R, [None] * R
+    scales = []
+    for g in range(len(offsets) - 1):
+        lo, hi = offsets[g], offsets[g + 1]
+        s = group_scale(x, lo, hi)
+        scales.append(s)
+        for r in range(lo, hi):
+            q[r], sb[r] = nv_row_under(x[r], s)
+    return q, sb, scales
+
+
+def nv_quantize_2d(x: Sequence[Sequence[int]], offsets: Sequence[int]):
+    """Rows of BF16 patterns (R and K multiples of 16, every group whole 16-row tiles) ->
+    (packed q rows, tile scales sb[R/16][K/16], [s_g])."""
+    R, K = len(x), len(x[0])
+    codes = [[None] * K for _ in range(R)]
+    sb = [[None] * (K // 16) for _ in range(R // 16)]
+    scales = []
+    for g in range(len(offsets) - 1):
+        lo, hi = offsets[g], offsets[g + 1]
+        assert lo % 16 == 0 and hi % 16 == 0
+        s = group_scale(x, lo, hi)
+        scales.append(s)
+        for tr in range(lo // 16, hi // 16):
+            for tc in range(K // 16):
+                cells = [(16 * tr + i, 16 * tc + j) for i in range(16) for j in range(16)]
+                code, c = nv_block([bf16_value(x[r][k]) for r, k in cells], s)
+                sb[tr][tc] = code
+                for (r, k), ck in zip(cells, c):
+                    codes[r][k] = ck
+    return [_pack(row) for row in codes], sb, scales
+
+
+def _nibble(q_rows, r: int, k: int) -> int:
+    byte = q_rows[r][k // 2]
+    return (byte >> 4) & 0xF if k % 2 else byte & 0xF
+
+
+def nv_dequantize_per_group(q_rows, sb_rows, scales, offsets):
+    """BF16 patterns RNE_BF16(fl(exact(DEC(q) * DEC(sb[r][k/16])) * s_g)) of the per-group
+    layout; scales are (sign, magnitude) pairs as binary32_value returns them."""
+    R, K = len(q_rows), 2 * len(q_rows[0])
+    y = [[None] * K for _ in range(R)]
+    for g in range(len(offsets) - 1):
+        sg, s = scales[g]
+        for r in range(offsets[g], offsets[g + 1]):
+            for k in range(K):
+                y[r][k] = nv_dequant_one(_nibble(q_rows, r, k), sb_rows[r][k // 16], sg, s)
+    return y
+
+
+def nv_dequantize_2d(q_rows, sb_tiles, scales, offsets):
+    """BF16 patterns of the 16x16-tile layout: every element of tile (tr, tc), in a row of
+    group g, is RNE_BF16(fl(exact(DEC(q) * DEC(sb[tr][tc])) * s_g))."""
+    R, K = len(q_rows), 2 * len(q_rows[0])
+    y = [[None] * K for _ in range(R)]
+    for g in range(len(offsets) - 1):
+        sg, s = scales[g]
+        for tr in range(offsets[g] // 16, offsets[g + 1] // 16):
+            for tc in range(K // 16):
+                t = sb_tiles[tr][tc]
+                for i in range(16):
+                    for j in range(16):
+                        r, k = 16 * tr + i, 16 * tc + j
+                        y[r][k] = nv_dequant_one(_nibble(q_rows, r, k), t, sg, s)
+    return y
 
 
 def nv_dequant_one(code: int, sb: int, s_t_sign: int, s_t) -> int:

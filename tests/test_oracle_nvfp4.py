@@ -427,3 +427,127 @@ def test_2d_rejects_partial_tiles():
     x = np.zeros((32, 32), np.uint16)
     assert oracle.nv_quantize_2d(x, [0, 8, 32])[3] is False              # group not whole tiles
     assert oracle.nv_quantize_2d(np.zeros((24, 32), np.uint16), [0, 24])[3] is False
+
+
+# --------------------------------------------------------------------------- 16x16 tiles and row groups
+# against the exact verifier and a hand-worked multi-tile fixture.  The C oracle walks rows
+# and looks up each row's group and tile; exact.py walks group -> tile -> element.  The
+# inputs span several tile rows and columns (sb not square) and several groups with
+# distinct scales, one of them empty, so a transposed tile lookup or a group walk shifted
+# by one row changes bytes (checked below on the same inputs).
+
+def _f32_scales(s):
+    return [exact.binary32_value(int(b)) for b in np.asarray(s, np.float32).view(np.uint32)]
+
+
+def _np_rows(rows, dtype):
+    return np.array(rows, dtype=dtype)
+
+
+def test_2d_multitile_dequant_golden():
+    g = _read_golden("nvfp4_2d_multitile.txt")              # strings: offsets are decimal
+    off = [int(v) for v in g["offsets"]]
+    s = np.array([int(v, 16) for v in g["group_scale_f32"]], np.uint32).view(np.float32)
+    q = np.full((32, 24), int(g["q_byte"][0], 16), np.uint8)
+    sb = np.array([[int(v, 16) for v in g["sb_row0"]], [int(v, 16) for v in g["sb_row1"]]], np.uint8)
+    y = oracle.nv_dequantize_2d(q, sb, s, off)
+    for tr in range(2):
+        even = [int(v, 16) for v in g["dequant_tilerow%d_even" % tr]]
+        odd = [int(v, 16) for v in g["dequant_tilerow%d_odd" % tr]]
+        for tc in range(3):
+            blk = y[16 * tr:16 * tr + 16, 16 * tc:16 * tc + 16]
+            assert np.all(blk[:, 0::2] == even[tc]), (tr, tc)
+            assert np.all(blk[:, 1::2] == odd[tc]), (tr, tc)
+    assert np.array_equal(_np_rows(exact.nv_dequantize_2d(q.tolist(), sb.tolist(), _f32_scales(s), off),
+                                   np.uint16), y)
+
+
+def _tile_scaled_rows(rng, R, K, log2_range=12):
+    """Random finite BF16 with every 16x16 tile scaled by its own power of two, so that
+    neighbouring tiles get different E4M3 scales."""
+    x = _rand_rows(rng, R, K)
+    x &= np.uint16(0x83FF)                                     # exponent field 0..7 ...
+    x |= np.uint16(0x3800)                                     # ... moved to 112..119
+    shift = rng.integers(-log2_range, log2_range + 1, size=(R // 16, K // 16))
+    e = ((x >> 7) & 0xFF).astype(np.int64) + np.repeat(np.repeat(shift, 16, 0), 16, 1)
+    return ((x & np.uint16(0x807F)) | (e.astype(np.uint16) << 7)).astype(np.uint16)
+
+
+def test_2d_quantize_multitile_multigroup_matches_exact():
+    rng = np.random.default_rng(51)
+    R, K = 48, 48
+    x = _tile_scaled_rows(rng, R, K)
+    x[16:32, 16:32] = 0                                        # an all-zero tile
+    x[32, 40] = 0x4528                                         # 2688 in group 2
+    off = [0, 16, 16, 48]                                      # an empty group in between
+    q, sb, s, ok = oracle.nv_quantize_2d(x, off)
+    assert ok and sb.shape == (3, 3)
+    eq, esb, es = exact.nv_quantize_2d(x.tolist(), off)
+    assert np.array_equal(q, _np_rows(eq, np.uint8))
+    assert np.array_equal(sb, _np_rows(esb, np.uint8))
+    assert [exact.binary32_value(int(b))[1] for b in s.view(np.uint32)] == es
+    assert len(set(sb.ravel().tolist())) >= 6                  # tile scales differ
+    assert len(set(s.tolist())) == 3                           # group scales differ
+    y = oracle.nv_dequantize_2d(q, sb, s, off)
+    assert np.array_equal(_np_rows(exact.nv_dequantize_2d(eq, esb, _f32_scales(s), off), np.uint16), y)
+
+
+def _random_2d_layout(seed):
+    rng = np.random.default_rng(seed)
+    R, K = 64, 48                                              # 4 x 3 tiles
+    q = rng.integers(0, 256, size=(R, K // 2), dtype=np.uint8)
+    q[(q & 0x7) == 0] |= np.uint8(0x1)                         # no zero codes: every value shows its scale
+    q[(q & 0x70) == 0] |= np.uint8(0x10)
+    sb = rng.integers(0x08, 0x7F, size=(R // 16, K // 16), dtype=np.uint8)
+    off = [0, 16, 16, 48, 64]
+    s = np.array([0.75, 1024.0, 3.0 * 2.0 ** -20, 2.0 ** 90], np.float32)
+    return q, sb, s, off
+
+
+def test_2d_dequant_of_random_bytes_matches_exact():
+    """Dequantization of arbitrary stored bytes (not only quantizer output): every tile scale
+    code 0x08..0x7E, every E2M1 code, four group scales (one group empty)."""
+    q, sb, s, off = _random_2d_layout(52)
+    y = oracle.nv_dequantize_2d(q, sb, s, off)
+    ey = exact.nv_dequantize_2d(q.tolist(), sb.tolist(), _f32_scales(s), off)
+    assert np.array_equal(_np_rows(ey, np.uint16), y)
+
+
+def test_2d_inputs_tell_the_plausible_index_mistakes_apart():
+    """The random layout above really exercises the tile lookup and the group walk: a tile
+    scale looked up transposed (flat index (k/16) * tiles_r + r/16), or a group walk that
+    gives each group's first row to the group before it, changes the bytes."""
+    q, sb, s, off = _random_2d_layout(52)
+    right = _np_rows(exact.nv_dequantize_2d(q.tolist(), sb.tolist(), _f32_scales(s), off), np.uint16)
+    tr, tc = sb.shape
+    sb_transposed_lookup = sb.ravel().reshape(tc, tr).T
+    wrong_tile = _np_rows(exact.nv_dequantize_2d(q.tolist(), sb_transposed_lookup.tolist(),
+                                                 _f32_scales(s), off), np.uint16)
+    assert not np.array_equal(wrong_tile, right)
+    sb_rows = np.repeat(sb, 16, axis=0).repeat(16, axis=1)[:, ::16]
+    shifted = [off[0]] + [o + 1 if 0 < o < off[-1] else o for o in off[1:]]
+    wrong_group = _np_rows(exact.nv_dequantize_per_group(q.tolist(), sb_rows.tolist(),
+                                                         _f32_scales(s), shifted), np.uint16)
+    assert not np.array_equal(wrong_group, right)
+
+
+def test_per_group_matches_exact():
+    rng = np.random.default_rng(53)
+    R, K = 40, 48
+    x = _rand_rows(rng, R, K)
+    x &= np.uint16(0x83FF)
+    x |= np.uint16(0x3800)                                     # magnitudes 2^-15 .. 2^-8
+    x[7:23] = (x[7:23] & np.uint16(0x807F)) | np.uint16(0x4400)    # group 2 far larger
+    x[23:30] = 0                                               # zero rows in group 3
+    x[35, 3] = 0x7F7F                                          # BF16 max in group 3
+    off = [0, 7, 7, 23, 40]
+    q, sb, s, ok = oracle.nv_quantize_per_group(x, off)
+    assert ok
+    eq, esb, es = exact.nv_quantize_per_group(x.tolist(), off)
+    assert np.array_equal(q, _np_rows(eq, np.uint8))
+    assert np.array_equal(sb, _np_rows(esb, np.uint8))
+    assert [exact.binary32_value(int(b))[1] for b in s.view(np.uint32)] == es
+    # the per-group dequant is the per-token one with each row's group scale
+    y = oracle.nv_dequantize(q, sb, np.repeat(s, np.diff(off)))
+    ey = exact.nv_dequantize_per_group(eq, esb, _f32_scales(s), off)
+    assert np.array_equal(_np_rows(ey, np.uint16), y)
