@@ -262,7 +262,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
+        "arithmetic": "bf16 in; binary32 IEEE scale and NVFP4 products, integer BF16-magnitude "
+                      "maxima and E8M0 codes; out E4M3/E8M0/E2M1 codes, f32 token scales, bf16 dequant",
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "bytes_per_step": bytes_step,
                    "elements_per_step": elems_step, "parallelism": "single GPU",

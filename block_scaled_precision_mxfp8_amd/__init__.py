@@ -152,8 +152,9 @@ def mx_quantize_mxfp8(x: torch.Tensor, mode="both", q_row=None, s_row=None, q_co
     M, K = x.shape
     _dev_tensor(x, "x", torch.bfloat16, (M, K))
     row, col = bool(m & MX_ROWWISE), bool(m & MX_COLWISE)
-    if K % 32 or (col and M % 32):
-        raise ValueError("MXFP8 needs K % 32 == 0 (and M % 32 == 0 for the columnwise copy)")
+    if (row and K % 32) or K % 8 or (col and M % 32):
+        raise ValueError("MXFP8 needs K % 32 == 0 for the rowwise copy, M % 32 == 0 and "
+                         "K % 8 == 0 for the columnwise copy")
     q_row = _out(q_row, "q_row", torch.uint8, (M, K), x) if row else None
     s_row = _out(s_row, "s_row", torch.uint8, (M, K // 32), x) if row else None
     q_col = _out(q_col, "q_col", torch.uint8, (K, M), x) if col else None

@@ -33,6 +33,15 @@ hipError_t launch_nv_quant_2d(const void* x, int64_t R, int64_t K, const int64_t
                               void* q, void* sb, float* s_group, int32_t* status, hipStream_t stream);
 hipError_t launch_nv_dequant_2d(const void* q, const void* sb, const float* s_group, const int64_t* off,
                                 int64_t G, int64_t R, int64_t K, void* y, hipStream_t stream);
+// Whether each launcher's grid fits one dispatch (next to the launchers' grid formulas).
+bool mx_quant_launch_fits(int64_t M, int64_t K, int mode);
+bool mx_quant_grouped_launch_fits(int64_t M, int64_t K);
+bool mx_dequant_launch_fits(int64_t rows, int64_t cols);
+bool nv_quant_launch_fits(int64_t R, int64_t K);
+bool nv_group_launch_fits(int64_t R, int64_t K, int64_t G);
+bool nv_2d_launch_fits(int64_t R, int64_t K, int64_t G);
+bool nv_dequant_launch_fits(int64_t R, int64_t K);
+bool nv_dequant_2d_launch_fits(int64_t R, int64_t K);
 }  // namespace bsq
 
 namespace {
@@ -90,8 +99,10 @@ int mx_quantize_mxfp8(const void* x, int64_t M, int64_t K, int mode, void* q_row
     if (mode != MX_ROWWISE && mode != MX_COLWISE && mode != MX_BOTH) return BSQ_ERR_MODE;
     const bool row = (mode & MX_ROWWISE) != 0, col = (mode & MX_COLWISE) != 0;
     if (!size_ok(M, K, 2)) return BSQ_ERR_SHAPE;
-    if (K % 32 != 0) return BSQ_ERR_SHAPE;
-    if (col && M % 32 != 0) return BSQ_ERR_SHAPE;
+    if (row && K % 32 != 0) return BSQ_ERR_SHAPE;       // rowwise blocks along K
+    if (K % 8 != 0) return BSQ_ERR_SHAPE;               // 16-byte rows (columnwise only)
+    if (col && M % 32 != 0) return BSQ_ERR_SHAPE;       // columnwise blocks along M
+    if (!bsq::mx_quant_launch_fits(M, K, mode)) return BSQ_ERR_SHAPE;
     if (M == 0 || K == 0) return BSQ_OK;
     if (x == nullptr) return BSQ_ERR_NULL;
     if (row && (q_row == nullptr || s_row == nullptr)) return BSQ_ERR_NULL;
@@ -120,6 +131,7 @@ int mx_quantize_mxfp8_grouped(const void* x, int64_t M, int64_t K, int mode,
     const int64_t min_blocks = (M + 31) / 32;
     if (min_blocks + E >= (int64_t(1) << 31)) return BSQ_ERR_SHAPE;
     if (s_ld < min_blocks || !size_ok(K, s_ld, 1)) return BSQ_ERR_SHAPE;
+    if (!bsq::mx_quant_grouped_launch_fits(M, K)) return BSQ_ERR_SHAPE;
     if (expert_offsets == nullptr) return BSQ_ERR_NULL;
     if (misaligned(expert_offsets, 8)) return BSQ_ERR_ALIGN;
     if (status_dev != nullptr && misaligned(status_dev, 4)) return BSQ_ERR_ALIGN;
@@ -149,6 +161,7 @@ static int nv_quant_common(const void* x, int64_t R, int64_t K, const int64_t* o
     if (!size_ok(R, K, 2)) return BSQ_ERR_SHAPE;
     if (K % 16 != 0) return BSQ_ERR_SHAPE;
     if (grouped && (E < 1 || E > INT64_MAX / 8 - 1)) return BSQ_ERR_SHAPE;
+    if (!bsq::nv_quant_launch_fits(R, K)) return BSQ_ERR_SHAPE;
     if (grouped && offsets == nullptr) return BSQ_ERR_NULL;
     if (grouped && misaligned(offsets, 8)) return BSQ_ERR_ALIGN;
     if (grouped && status != nullptr && misaligned(status, 4)) return BSQ_ERR_ALIGN;
@@ -187,6 +200,7 @@ int nv_quantize_nvfp4_per_token_scatter(const void* h, int64_t T, int64_t K, con
     if (!size_ok(T, K, 2) || !size_ok(N, K, 2)) return BSQ_ERR_SHAPE;
     if (K % 16 != 0) return BSQ_ERR_SHAPE;
     if (top_k < 1 || !size_ok(T, top_k, 8)) return BSQ_ERR_SHAPE;
+    if (!bsq::nv_quant_launch_fits(T, K)) return BSQ_ERR_SHAPE;
     if (status_dev != nullptr && misaligned(status_dev, 4)) return BSQ_ERR_ALIGN;
     const bool no_rows = (T == 0 || K == 0);
     if (no_rows && status_dev == nullptr) return BSQ_OK;
@@ -214,6 +228,7 @@ int nv_quantize_nvfp4_per_group(const void* x, int64_t R, int64_t K, const int64
     if (!size_ok(R, K, 2)) return BSQ_ERR_SHAPE;
     if (K % 16 != 0) return BSQ_ERR_SHAPE;
     if (G < 1 || G > INT64_MAX / 8 - 1) return BSQ_ERR_SHAPE;
+    if (!bsq::nv_group_launch_fits(R, K, G)) return BSQ_ERR_SHAPE;
     if (group_offsets == nullptr || s_group == nullptr) return BSQ_ERR_NULL;
     if (misaligned(group_offsets, 8) || misaligned(s_group, 16)) return BSQ_ERR_ALIGN;
     if (status_dev != nullptr && misaligned(status_dev, 4)) return BSQ_ERR_ALIGN;
@@ -236,6 +251,7 @@ int nv_dequantize_per_group(const void* q, const void* sb, const float* s_group,
     if (!size_ok(R, K, 2)) return BSQ_ERR_SHAPE;
     if (K % 16 != 0) return BSQ_ERR_SHAPE;
     if (G < 1 || G > INT64_MAX / 8 - 1) return BSQ_ERR_SHAPE;
+    if (!bsq::nv_dequant_launch_fits(R, K)) return BSQ_ERR_SHAPE;
     if (R == 0 || K == 0) return BSQ_OK;
     if (q == nullptr || sb == nullptr || s_group == nullptr || group_offsets == nullptr || y == nullptr)
         return BSQ_ERR_NULL;
@@ -255,6 +271,7 @@ int nv_quantize_nvfp4_2d(const void* x, int64_t R, int64_t K, const int64_t* gro
     if (!size_ok(R, K, 2)) return BSQ_ERR_SHAPE;
     if (R % 16 != 0 || K % 16 != 0) return BSQ_ERR_SHAPE;
     if (G < 1 || G > INT64_MAX / 8 - 1) return BSQ_ERR_SHAPE;
+    if (!bsq::nv_2d_launch_fits(R, K, G)) return BSQ_ERR_SHAPE;
     if (group_offsets == nullptr || s_group == nullptr) return BSQ_ERR_NULL;
     if (misaligned(group_offsets, 8) || misaligned(s_group, 16)) return BSQ_ERR_ALIGN;
     if (status_dev != nullptr && misaligned(status_dev, 4)) return BSQ_ERR_ALIGN;
@@ -276,6 +293,7 @@ int nv_dequantize_2d(const void* q, const void* sb, const float* s_group, const 
     if (!size_ok(R, K, 2)) return BSQ_ERR_SHAPE;
     if (R % 16 != 0 || K % 16 != 0) return BSQ_ERR_SHAPE;
     if (G < 1 || G > INT64_MAX / 8 - 1) return BSQ_ERR_SHAPE;
+    if (!bsq::nv_dequant_2d_launch_fits(R, K)) return BSQ_ERR_SHAPE;
     if (R == 0 || K == 0) return BSQ_OK;
     if (q == nullptr || sb == nullptr || s_group == nullptr || group_offsets == nullptr || y == nullptr)
         return BSQ_ERR_NULL;
@@ -294,6 +312,7 @@ int mx_dequantize(const void* q, const void* s, int64_t rows, int64_t cols, void
                   void* stream) {
     if (!size_ok(rows, cols, 2)) return BSQ_ERR_SHAPE;
     if (cols % 32 != 0) return BSQ_ERR_SHAPE;
+    if (!bsq::mx_dequant_launch_fits(rows, cols)) return BSQ_ERR_SHAPE;
     if (rows == 0 || cols == 0) return BSQ_OK;
     if (q == nullptr || s == nullptr || y == nullptr) return BSQ_ERR_NULL;
     if (misaligned(q, 16) || misaligned(s, 16) || misaligned(y, 16)) return BSQ_ERR_ALIGN;
@@ -307,6 +326,7 @@ int nv_dequantize(const void* q, const void* sb, const float* st, int64_t R, int
                   void* stream) {
     if (!size_ok(R, K, 2)) return BSQ_ERR_SHAPE;
     if (K % 16 != 0) return BSQ_ERR_SHAPE;
+    if (!bsq::nv_dequant_launch_fits(R, K)) return BSQ_ERR_SHAPE;
     if (R == 0 || K == 0) return BSQ_OK;
     if (q == nullptr || sb == nullptr || st == nullptr || y == nullptr) return BSQ_ERR_NULL;
     if (misaligned(q, 16) || misaligned(sb, 16) || misaligned(st, 16) || misaligned(y, 16))

@@ -165,6 +165,16 @@ __device__ __forceinline__ uint32_t fastdiv(uint32_t n, const FastDiv& f) {
     return (uint32_t)(t >> 32);
 }
 
+// ----------------------------------------------------------------------------- launch limits
+
+// Whether one launch of `workgroups` x `threads` can be dispatched: the x dimension of a
+// grid holds at most 2^31 - 1 workgroups, and the dispatch packet counts the grid's
+// work-items in 32 bits.  Each launcher states its grid through a *_launch_fits function
+// that the C ABI calls before launching anything.
+inline bool dispatch_fits(int64_t workgroups, int64_t threads) {
+    return workgroups >= 0 && workgroups < (int64_t(1) << 31) && workgroups * threads < (int64_t(1) << 32);
+}
+
 // ----------------------------------------------------------------------------- streaming access
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));

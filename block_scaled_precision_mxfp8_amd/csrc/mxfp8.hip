@@ -1101,6 +1101,21 @@ hipError_t launch_mx_quant(const void* x, int64_t M, int64_t K, int mode,
     return hipGetLastError();
 }
 
+// The grids of launch_mx_quant / launch_mx_quant_grouped / launch_mx_dequant fit one dispatch?
+bool mx_quant_launch_fits(int64_t M, int64_t K, int mode) {
+    if (mode == 1) {
+        const int64_t tiles = (M * K / 8 + 64 * ROW_SLOTS - 1) / (64 * ROW_SLOTS);
+        return dispatch_fits((tiles + ROW_WAVES - 1) / ROW_WAVES, 64 * ROW_WAVES);
+    }
+    const int64_t n_wg = ((M + LibTile::ROWS - 1) / LibTile::ROWS) * ((K + LibTile::COLS - 1) / LibTile::COLS);
+    if (mode == 2 && n_wg > 2 * TILE_PERSISTENT_WGS) return true;   // persistent grid
+    return dispatch_fits(n_wg, LibTile::THREADS);
+}
+
+bool mx_quant_grouped_launch_fits(int64_t M, int64_t K) {
+    return dispatch_fits((M + WIN_ROWS - 1) / WIN_ROWS * ((K + 255) / 256), 256);
+}
+
 template <int SLOTS>
 static void launch_mx_dequant_slots(const void* q, const void* s, int64_t rows, int64_t cols,
                                     void* y, hipStream_t stream) {
@@ -1115,6 +1130,12 @@ static void launch_mx_dequant_slots(const void* q, const void* s, int64_t rows, 
 // Measured: 8192 x 2048 12.6 -> 11.9 us, 2048 x 6144 10.2 -> 9.2 us; at 196608 x 2048 two
 // slots stay faster (194 against 204 us), at 65536 x 2048 the two are level (67.0, 67.6).
 constexpr int64_t MX_DQ_SMALL_CHUNKS = int64_t(1) << 22;
+
+bool mx_dequant_launch_fits(int64_t rows, int64_t cols) {
+    const int64_t n_chunks = rows * cols / 8;
+    const int64_t slots = n_chunks <= MX_DQ_SMALL_CHUNKS ? 8 : MX_DQ_SLOTS;
+    return dispatch_fits((n_chunks + 256 * slots - 1) / (256 * slots), 256);
+}
 
 hipError_t launch_mx_dequant(const void* q, const void* s, int64_t rows, int64_t cols,
                              void* y, hipStream_t stream) {

@@ -775,6 +775,38 @@ static void launch_rows(const void* x, int64_t R, int64_t K, void* q, void* sb, 
 #endif
 constexpr int64_t NV_PAIR_MAX_K = BSQ_NV_PAIR_MAX_K;
 
+// Workgroups of the per-row quantizers (per-token, grouped, per-group pass 2, scatter):
+// one wave per span of two rows up to NV_PAIR_MAX_K, of one row above.
+static int64_t nv_rows_grid(int64_t R, int64_t K) {
+    const int64_t rpw = K <= NV_PAIR_MAX_K ? 2 : 1;
+    return ((R + rpw - 1) / rpw + NV_WAVES - 1) / NV_WAVES;
+}
+
+// The grids of the launchers below fit one dispatch?
+bool nv_quant_launch_fits(int64_t R, int64_t K) { return dispatch_fits(nv_rows_grid(R, K), 64 * NV_WAVES); }
+
+bool nv_group_launch_fits(int64_t R, int64_t K, int64_t G) {
+    return nv_quant_launch_fits(R, K) && dispatch_fits((G + 255) / 256, 256);
+}
+
+bool nv_2d_launch_fits(int64_t R, int64_t K, int64_t G) {
+    const int64_t strips = (R / 16) * ((K + NV2D_COLS - 1) / NV2D_COLS);
+    return dispatch_fits((strips + NV_WAVES - 1) / NV_WAVES, 64 * NV_WAVES) && dispatch_fits((G + 255) / 256, 256);
+}
+
+// The dequantizers index half blocks (8 codes) with 32 bits and split a tensor into row
+// ranges of at most 2^31 half blocks: a row must fit in one range (whole 16-row tiles for
+// the 16x16 layout).
+bool nv_dequant_launch_fits(int64_t R, int64_t K) {
+    (void)R;
+    return K / 8 <= (int64_t(1) << 31);
+}
+
+bool nv_dequant_2d_launch_fits(int64_t R, int64_t K) {
+    (void)R;
+    return 16 * (K / 8) <= (int64_t(1) << 31);
+}
+
 hipError_t launch_nv_quant(const void* x, int64_t R, int64_t K, void* q, void* sb, float* st,
                            const int64_t* offsets, int64_t E, int32_t* status,
                            hipStream_t stream) {

@@ -26,7 +26,11 @@
  *  - Argument errors are detected on the host before anything is launched and are
  *    returned synchronously; outputs are then untouched:
  *      BSQ_ERR_NULL    a required pointer is NULL (or a pointer the mode needs is missing)
- *      BSQ_ERR_SHAPE   a size is negative or violates the divisibility rule of the call
+ *      BSQ_ERR_SHAPE   a size is negative, violates the divisibility rule of the call, or
+ *                      is too large for one kernel launch (a launch holds fewer than 2^32
+ *                      threads: e.g. per-token NVFP4 takes 32 threads per row up to K = 768
+ *                      and 64 above, MXFP8 dequant one per 16 elements; the dequantizers
+ *                      need K <= 2^34, the 16x16-tile one K <= 2^30)
  *      BSQ_ERR_ALIGN   a tensor pointer is not 16-byte aligned
  *      BSQ_ERR_MODE    unknown mode
  *      BSQ_ERR_ALIAS   two of the call's buffers overlap
@@ -70,9 +74,10 @@ enum bsq_mx_mode { MX_ROWWISE = 1, MX_COLWISE = 2, MX_BOTH = 3 };
  * mode MX_ROWWISE: blocks of 32 along K.  Needs K % 32 == 0.
  *   q_row u8 [M][K] E4M3,   s_row u8 [M][K/32] E8M0.
  * mode MX_COLWISE: blocks of 32 consecutive rows of one column, stored transposed so each
- *   block is contiguous.  Needs M % 32 == 0 and K % 32 == 0.
+ *   block is contiguous.  Needs M % 32 == 0, and K % 8 == 0 (rows of x are whole 16-byte
+ *   pieces; the blocks themselves put no condition on K).
  *   q_col u8 [K][M] E4M3,   s_col u8 [K][M/32] E8M0.
- * mode MX_BOTH: both copies from one read of x (same conditions as COLWISE).
+ * mode MX_BOTH: both copies from one read of x (M % 32 == 0 and K % 32 == 0).
  * Pointers of the copy a mode does not produce are ignored and may be NULL.
  */
 int mx_quantize_mxfp8(const void* x_bf16, int64_t M, int64_t K, int mode,

@@ -287,8 +287,9 @@ def _mx_defective_call(draw):
     if defect == "mode":
         args["mode"] = draw(st.sampled_from([0, 4, 5, -1, 7]))
         want = bsq.BSQ_ERR_MODE
-    elif defect == "k_mod":
-        args["K"] = K + draw(st.integers(1, 31))
+    elif defect == "k_mod":                             # rowwise/dual: K % 32; columnwise: K % 8
+        d = draw(st.integers(1, 31))
+        args["K"] = K + (d if mode != 2 or d % 8 else d + 1)
         want = bsq.BSQ_ERR_SHAPE
     elif defect == "m_mod":
         args["mode"] = draw(st.sampled_from([2, 3]))
@@ -319,3 +320,42 @@ def _mx_defective_call(draw):
 def test_mx_quant_rejects_every_single_defect(L, call):
     args, want = call
     assert mxq(L, **args) == want, args
+
+
+def test_mx_colwise_needs_only_m_multiple_of_32_and_16_byte_rows(L):
+    """The columnwise copy's blocks run along M, so K only has to give 16-byte rows
+    (K % 8 == 0); the rowwise and dual modes keep K % 32 == 0.  Zero M: nothing launches."""
+    for K in (8, 40, 72, 6184):
+        assert mxq(L, M=0, K=K, mode=2) == bsq.BSQ_OK, K
+        assert mxq(L, M=0, K=K, mode=1) == bsq.BSQ_ERR_SHAPE, K
+        assert mxq(L, M=0, K=K, mode=3) == bsq.BSQ_ERR_SHAPE, K
+    for K in (4, 36, 6180):
+        assert mxq(L, M=0, K=K, mode=2) == bsq.BSQ_ERR_SHAPE, K
+    assert mxq(L, M=48, K=40, mode=2) == bsq.BSQ_ERR_SHAPE      # M % 32 still applies
+
+
+def test_calls_too_large_for_one_launch_are_shape_errors(L):
+    """A launch holds fewer than 2^32 threads and the dequantizers split a tensor into row
+    ranges of at most 2^31 half blocks; sizes beyond either are rejected before any launch
+    (the host sizes only, no memory behind the fake pointers)."""
+    big = 2 ** 26
+    # per-token NVFP4: 64 threads a row above K = 768, 32 at or below
+    assert L.nv_quantize_nvfp4_per_token(A, big, 1024, B, C, D, None) == bsq.BSQ_ERR_SHAPE
+    assert L.nv_quantize_nvfp4_per_token(A, 2 * big, 768, B, C, D, None) == bsq.BSQ_ERR_SHAPE
+    assert L.nv_quantize_nvfp4_per_token_grouped(A, big, 1024, E_, 1, B, C, D, None, None) == bsq.BSQ_ERR_SHAPE
+    assert L.nv_quantize_nvfp4_per_token_scatter(A, big, 1024, E_, 1, 16, B, C, D, None, None) == bsq.BSQ_ERR_SHAPE
+    assert L.nv_quantize_nvfp4_per_group(A, big, 1024, E_, 1, B, C, D, None, None) == bsq.BSQ_ERR_SHAPE
+    assert L.nv_quantize_nvfp4_2d(A, 2 ** 22, 2 ** 16, E_, 1, B, C, D, None, None) == bsq.BSQ_ERR_SHAPE
+    # MXFP8: rowwise one thread per 64 elements, dual one per 128, dequant one per 16
+    assert mxq(L, M=2 ** 22, K=2 ** 16, mode=1) == bsq.BSQ_ERR_SHAPE
+    assert mxq(L, M=2 ** 23, K=2 ** 16, mode=3) == bsq.BSQ_ERR_SHAPE
+    assert L.mx_dequantize(A, B, 2 ** 20, 2 ** 16, C, None) == bsq.BSQ_ERR_SHAPE
+    assert L.mx_quantize_mxfp8_grouped(A, 2 ** 23, 2 ** 16, 2, E_, 1, B, C, D, F_, 2 ** 18, None,
+                                       None) == bsq.BSQ_ERR_SHAPE
+    # dequantizers: K / 8 half blocks of a row within one range (whole 16-row tiles for 2-D)
+    assert L.nv_dequantize(A, B, C, 0, 2 ** 34, D, None) == bsq.BSQ_OK
+    assert L.nv_dequantize(A, B, C, 0, 2 ** 35, D, None) == bsq.BSQ_ERR_SHAPE
+    assert L.nv_dequantize_per_group(A, B, C, E_, 1, 0, 2 ** 35, D, None) == bsq.BSQ_ERR_SHAPE
+    assert L.nv_dequantize_2d(A, B, C, E_, 1, 0, 2 ** 30, D, None) == bsq.BSQ_OK
+    assert L.nv_dequantize_2d(A, B, C, E_, 1, 0, 2 ** 31, D, None) == bsq.BSQ_ERR_SHAPE
+    assert L.nv_dequantize_2d(A, B, C, E_, 1, 16, 2 ** 31, D, None) == bsq.BSQ_ERR_SHAPE

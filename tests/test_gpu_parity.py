@@ -61,6 +61,22 @@ def test_mx_colwise_and_both_match_oracle(M, K, mode):
         assert np.all(qr.payload() == 0xA5) and np.all(sr.payload() == 0xA5)
 
 
+@pytest.mark.parametrize("M,K", [(64, 8), (96, 40), (160, 72), (64, 6184), (8192, 4104)])
+def test_mx_colwise_with_k_not_a_multiple_of_32(M, K):
+    """The columnwise copy's blocks run along M, so it takes any K of whole 16-byte rows:
+    the tile's last column group is ragged at 8-column granularity (and 8192 x 4104 runs
+    the persistent form, 1088 tiles)."""
+    log("mx colwise %dx%d" % (M, K))
+    x = mixed_bf16(np.random.default_rng(M * 131 + K), M, K)
+    qr, sr, qc, sc = _mx_gpu(x, bsq.MX_COLWISE)
+    eqc, esc = oracle.mx_quantize_colwise(x)
+    assert_same("q_col", qc.payload().reshape(K, M), eqc)
+    assert_same("s_col", sc.payload().reshape(K, M // 32), esc)
+    assert np.all(qr.payload() == 0xA5) and np.all(sr.payload() == 0xA5)
+    y = bsq.mx_dequantize(torch.from_numpy(eqc).cuda(), torch.from_numpy(esc).cuda())
+    assert_same("dequant", bits(y), oracle.mx_dequantize(eqc, esc))
+
+
 def test_mx_both_on_a_tensor_with_tiles_beyond_31_bit_offsets():
     """M = 2^23 + 32 rows: a workgroup tile of the columnwise copy then spans more than
     2^31 bytes of q_col, so the kernel addresses with 64-bit offsets (and the tile grid
