@@ -94,11 +94,13 @@ def parse():
 
 
 PROFILE_OPS = ("per_group_quant", "per_group_dequant", "tile16_quant", "tile16_dequant",
-               "scatter", "grouped_dual", "grouped_colwise")
+               "scatter", "grouped_dual", "grouped_colwise", "workload2", "workload4")
 
 
 def profile_op(torch, bsq, workloads, dev, op):
-    """One extended op, twice, after a 1 GiB copy, for rocprofv3 counter passes: the
+    """One op, twice, after a 1 GiB copy, for rocprofv3 counter passes: the ops of workload
+    2 (MXFP8 dual quant of 8192 x 2048 and both dequants) and of workload 4 (per-row NVFP4
+    and rowwise MXFP8 of the stacked gate_up and down weights, with their dequants), the
     per-expert-scale and 16x16-tile NVFP4 export of the stacked gate_up weights (196608 x
     2048, 128 groups), quantize-then-scatter of 65536 tokens to 8 routed rows each, and
     grouped MXFP8 of 524288 x 2048 rows over 128 experts with Zipf(1.1) top-8 routing."""
@@ -106,7 +108,36 @@ def profile_op(torch, bsq, workloads, dev, op):
     u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
     src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)
     dst = torch.empty_like(src)
-    if op.startswith(("per_group", "tile16")):
+    if op == "workload2":
+        # MXFP8 dual quant of the 8192 x 2048 activations, dequant of both copies
+        x = torch.from_numpy(workloads.config2()["x"].view(np.int16)).view(bf).to(dev)
+        M, K = x.shape
+        out = (torch.empty(M, K, dtype=u8, device=dev), torch.empty(M, K // 32, dtype=u8, device=dev),
+               torch.empty(K, M, dtype=u8, device=dev), torch.empty(K, M // 32, dtype=u8, device=dev))
+        yr, yc = torch.empty(M, K, dtype=bf, device=dev), torch.empty(K, M, dtype=bf, device=dev)
+
+        def fn():
+            bsq.mx_quantize_mxfp8(x, "both", *out)
+            bsq.mx_dequantize(out[0], out[1], yr)
+            bsq.mx_dequantize(out[2], out[3], yc)
+    elif op == "workload4":
+        # per-row NVFP4 and rowwise MXFP8 of the stacked expert weights, and their dequant
+        ws = [(torch.randn(M, K, device=dev) * 0.02).to(bf) for M, K in ((196608, 2048), (262144, 768))]
+        bufs = []
+        for w in ws:
+            M, K = w.shape
+            bufs.append(((torch.empty(M, K // 2, dtype=u8, device=dev), torch.empty(M, K // 16, dtype=u8, device=dev),
+                          torch.empty(M, dtype=f32, device=dev)),
+                         (torch.empty(M, K, dtype=u8, device=dev), torch.empty(M, K // 32, dtype=u8, device=dev)),
+                         torch.empty(M, K, dtype=bf, device=dev)))
+
+        def fn():
+            for w, (nv_out, mx_out, y) in zip(ws, bufs):
+                bsq.nv_quantize_nvfp4_per_token(w, *nv_out)
+                bsq.nv_dequantize(*nv_out, y)
+                bsq.mx_quantize_mxfp8(w, "rowwise", *mx_out)
+                bsq.mx_dequantize(*mx_out, y)
+    elif op.startswith(("per_group", "tile16")):
         M, K, rows = 196608, 2048, 1536
         w = (torch.randn(M, K, device=dev) * 0.02).to(bf)
         off = torch.arange(0, M + 1, rows, dtype=torch.int64, device=dev)

@@ -22,21 +22,57 @@ namespace bsq {
 // Cache policy of each kernel family's one-touch accesses: bit 0 = non-temporal loads,
 // bit 1 = non-temporal stores.  Measured on the layer-step stream (MX dual, NV quant,
 // dequants back to back): non-temporal loads speed up the read-heavy kernels in isolation
-// (rowwise 206 -> 184 us on 196608 x 2048) but slow the dual kernel; non-temporal stores
-// leave no dirty Infinity-Cache lines for the next kernel to write back, which speeds up
-// the stream (5623 -> 6001 GB/s per step) at some cost to a write-heavy kernel timed alone.
+// (rowwise 206 -> 184 us on 196608 x 2048); non-temporal stores leave no dirty
+// Infinity-Cache lines for the next kernel to write back, which speeds up the stream (5623
+// -> 6001 GB/s per step) at some cost to a write-heavy kernel timed alone.  The tile
+// kernels take non-temporal loads too: the dual kernel alone is unchanged (101.5 against
+// 100.5 us on 65536 x 2048, 14.3 against 14.5 on 8192 x 2048), the columnwise mode 1%
+// faster (627 against 634 us on 524288 x 2048), the read that follows either kernel 7 us
+// faster, and the step 6141-6147 against 6131-6139 GB/s.  Non-temporal stores carry only
+// whole lines: the scale bytes (8 or 4 per row or column of a workgroup tile) use ordinary
+// stores, so that pieces of one line written by different workgroups meet in the caches;
+// stored non-temporally they made the dual kernel 40% slower (141 against 101 us).
 #ifndef BSQ_POLICY_MXROW
 #define BSQ_POLICY_MXROW 3
 #endif
 #ifndef BSQ_POLICY_MXTILE
-#define BSQ_POLICY_MXTILE 2
+#define BSQ_POLICY_MXTILE 3
 #endif
 #ifndef BSQ_POLICY_MXDQ
 #define BSQ_POLICY_MXDQ 2
 #endif
+// The grouped kernel reads the rows of a block that reaches past its window a second time,
+// mostly from the caches, so its loads keep the ordinary policy.
+#ifndef BSQ_POLICY_MXGRP
+#define BSQ_POLICY_MXGRP 2
+#endif
 constexpr bool MXROW_NT_LOAD = (BSQ_POLICY_MXROW & 1) != 0, MXROW_NT_STORE = (BSQ_POLICY_MXROW & 2) != 0;
 constexpr bool MXTILE_NT_LOAD = (BSQ_POLICY_MXTILE & 1) != 0, MXTILE_NT_STORE = (BSQ_POLICY_MXTILE & 2) != 0;
+constexpr bool MXGRP_NT_LOAD = (BSQ_POLICY_MXGRP & 1) != 0, MXGRP_NT_STORE = (BSQ_POLICY_MXGRP & 2) != 0;
 constexpr bool MXDQ_NT_LOAD = (BSQ_POLICY_MXDQ & 1) != 0, MXDQ_NT_STORE = (BSQ_POLICY_MXDQ & 2) != 0;
+
+// A workgroup writes the rows of the columnwise copy q_col [K][M] it covers as one run of
+// bytes per column.  When M is a multiple of 128 the runs cover whole lines; when it is not,
+// the first and last line of a run are shared with the run of the workgroup holding the
+// neighbouring rows, and pieces of one line stored non-temporally reach HBM as separate
+// partial writes.  So a 16-byte piece goes non-temporal only if its whole 128-byte line lies
+// inside the run [run0, run1); the pieces of shared lines use ordinary stores and meet in the
+// caches first (the neighbouring row window is col_groups workgroups later, on the same XCD
+// when col_groups is a multiple of 8).  Measured with M % 128 = 32, each kernel timed
+// together with the 512 MiB read that follows it (the read's own time subtracted): dual
+// 65568 x 2048 137.5 -> 112.4 us, columnwise 1012 -> 749 us on 524320 x 2048, grouped dual /
+// columnwise on 524192 Zipf-routed rows 1182 / 940 -> 919 / 716 us; aligned shapes
+// unchanged.  The rowwise copy keeps non-temporal stores throughout: with K % 128 = 32 the
+// same rule made the dual kernel slower (129.8 -> 135.3 us on 65536 x 2080), the pieces of
+// a shared q_row line coming from workgroups on different XCDs.
+template <bool NT>
+__device__ __forceinline__ void st_run(uint4* p, const uint4& v, const uint8_t* run0, const uint8_t* run1) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p) & ~(uintptr_t)127;
+    if (NT && a >= reinterpret_cast<uintptr_t>(run0) && a + 128 <= reinterpret_cast<uintptr_t>(run1))
+        st_stream<true>(p, v);
+    else
+        st_stream<false>(p, v);
+}
 
 // ----------------------------------------------------------------------------- encode
 
@@ -390,8 +426,16 @@ __device__ __forceinline__ void process_tile(uint4 (&v)[16], int64_t M, int64_t 
             *reinterpret_cast<uint4*>(&lds_c[t.lcol + 2 * d][t.lrow]) = a;
             *reinterpret_cast<uint4*>(&lds_c[t.lcol + 2 * d + 1][t.lrow]) = b;
         } else if (ok) {
-            st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(qc + (2 * d) * M + t.co), a);
-            st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(qc + (2 * d + 1) * M + t.co), b);
+            uint8_t* ra = qc + (int64_t)(t.lcol + 2 * d) * M;     // this column's run: the tile's rows
+            uint8_t* rb = ra + M;
+            const int64_t rn = min((int64_t)G::ROWS, M - rw);
+            if (FULL) {
+                st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(qc + (2 * d) * M + t.co), a);
+                st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(qc + (2 * d + 1) * M + t.co), b);
+            } else {
+                st_run<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(qc + (2 * d) * M + t.co), a, ra, ra + rn);
+                st_run<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(qc + (2 * d + 1) * M + t.co), b, rb, rb + rn);
+            }
         }
         lds_scol[t.lcol + 2 * d][t.lrow >> 5] = (uint8_t)code0;      // the lane pair writes
         lds_scol[t.lcol + 2 * d + 1][t.lrow >> 5] = (uint8_t)code1;  // one value each
@@ -407,7 +451,11 @@ __device__ __forceinline__ void process_tile(uint4 (&v)[16], int64_t M, int64_t 
             const int c = idx / PARTS, part = idx % PARTS;
             const uint4 val = *reinterpret_cast<const uint4*>(&lds_c[c][16 * part]);
             if (FULL || (kw + c < K && rw + 16 * part < M))
-                st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(qc + (int64_t)c * M + 16 * part), val);
+            {
+                uint8_t* run = qc + (int64_t)c * M;
+                if (FULL) st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(run + 16 * part), val);
+                else st_run<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(run + 16 * part), val, run, run + min((int64_t)G::ROWS, M - rw));
+            }
         }
     }
     if (ROW) store_rowwise_tile<G, FULL>(M, K, rw, kw, q_row, s_row, lds_srow, lds_q);
@@ -733,8 +781,11 @@ __device__ __forceinline__ void dw_put(uint32_t (*bmax)[TILE_COLS], int j, int l
 
 typedef uint32_t u32x4u_t __attribute__((ext_vector_type(4), aligned(1)));
 
+#ifndef BSQ_GRP_WGS_PER_CU
+#define BSQ_GRP_WGS_PER_CU 3
+#endif
 template <bool FULL, bool ROWWISE>
-__global__ __launch_bounds__(256, 3)
+__global__ __launch_bounds__(256, BSQ_GRP_WGS_PER_CU)
 void mx_quant_grouped_window_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                          const int64_t* __restrict__ off, int64_t E,
                                          uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
@@ -788,7 +839,7 @@ void mx_quant_grouped_window_kernel(const uint16_t* __restrict__ x, int64_t M, i
             for (int t = 0; t < 4; ++t) {
                 const int idx = 4 * g + t;             // entry of the list [hs, w0) ++ [w1, te)
                 const int64_t r = idx < nh ? hs + idx : idx < nh + nt ? w1 + (idx - nh) : w0;
-                e[t] = ld_stream<MXTILE_NT_LOAD>(reinterpret_cast<const uint4*>(xc + r * K));
+                e[t] = ld_stream<MXGRP_NT_LOAD>(reinterpret_cast<const uint4*>(xc + r * K));
             }
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -806,8 +857,8 @@ void mx_quant_grouped_window_kernel(const uint16_t* __restrict__ x, int64_t M, i
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int64_t rh = w0 - 32 + 4 * g + t, rt = w1 + 4 * g + t;
-                eh[t] = ld_stream<MXTILE_NT_LOAD>(reinterpret_cast<const uint4*>(xc + (head && rh >= hs ? rh : w0) * K));
-                et[t] = ld_stream<MXTILE_NT_LOAD>(reinterpret_cast<const uint4*>(xc + (tail && rt < te ? rt : w0) * K));
+                eh[t] = ld_stream<MXGRP_NT_LOAD>(reinterpret_cast<const uint4*>(xc + (head && rh >= hs ? rh : w0) * K));
+                et[t] = ld_stream<MXGRP_NT_LOAD>(reinterpret_cast<const uint4*>(xc + (tail && rt < te ? rt : w0) * K));
             }
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -822,7 +873,7 @@ void mx_quant_grouped_window_kernel(const uint16_t* __restrict__ x, int64_t M, i
         uint4 v[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            v[i] = ld_stream<MXTILE_NT_LOAD>(reinterpret_cast<const uint4*>(xc + (i < hi ? r0 + i : w0) * K));
+            v[i] = ld_stream<MXGRP_NT_LOAD>(reinterpret_cast<const uint4*>(xc + (i < hi ? r0 + i : w0) * K));
         // rowwise codes, staged in LDS
 #pragma unroll
         for (int i = 0; i < 16 && ROWWISE; ++i) {
@@ -881,9 +932,19 @@ void mx_quant_grouped_window_kernel(const uint16_t* __restrict__ x, int64_t M, i
             if (colok && hi > 0) {
                 uint8_t* pa = q_col + (col + 2 * d) * M + r0;
                 uint8_t* pb = pa + M;
+                // the window's run of this column: rows w0 .. min(w1, M) - 1; a 16-byte piece
+                // goes non-temporal only inside a line the run covers whole (see st_run)
+                const uintptr_t la = reinterpret_cast<uintptr_t>(pa) & ~(uintptr_t)127;
+                const uintptr_t lb = reinterpret_cast<uintptr_t>(pb) & ~(uintptr_t)127;
+                const uintptr_t ra0 = reinterpret_cast<uintptr_t>(pa) - (uintptr_t)(r0 - w0);
+                const uintptr_t rlen = (uintptr_t)(FULL ? WIN_ROWS : min<int64_t>(WIN_ROWS, M - w0));
+                const bool nta = FULL || (la >= ra0 && la + 128 <= ra0 + rlen);
+                const bool ntb = FULL || (lb >= ra0 + M && lb + 128 <= ra0 + M + rlen);
                 if (hi == 16) {
-                    __builtin_nontemporal_store(u32x4_t{a.x, a.y, a.z, a.w}, reinterpret_cast<u32x4u_t*>(pa));
-                    __builtin_nontemporal_store(u32x4_t{bo.x, bo.y, bo.z, bo.w}, reinterpret_cast<u32x4u_t*>(pb));
+                    if (nta) __builtin_nontemporal_store(u32x4_t{a.x, a.y, a.z, a.w}, reinterpret_cast<u32x4u_t*>(pa));
+                    else __builtin_memcpy(pa, &a, 16);
+                    if (ntb) __builtin_nontemporal_store(u32x4_t{bo.x, bo.y, bo.z, bo.w}, reinterpret_cast<u32x4u_t*>(pb));
+                    else __builtin_memcpy(pb, &bo, 16);
                 } else {
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
@@ -922,7 +983,7 @@ void mx_quant_grouped_window_kernel(const uint16_t* __restrict__ x, int64_t M, i
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int ri = min(16 * half + i, last);
-                    v[i] = ld_stream<MXTILE_NT_LOAD>(reinterpret_cast<const uint4*>(xc + (bstart + ri) * K));
+                    v[i] = ld_stream<MXGRP_NT_LOAD>(reinterpret_cast<const uint4*>(xc + (bstart + ri) * K));
                 }
                 const int vc = min(max(blen - 16 * half, 0), 16);
                 const int ilo = (int)max<int64_t>(w0 - r0, 0);
@@ -980,7 +1041,7 @@ void mx_quant_grouped_window_kernel(const uint16_t* __restrict__ x, int64_t M, i
         const int r = idx / CHUNKS, c16 = idx % CHUNKS;
         if (FULL || kw + 16 * c16 < K) {
             const uint4 val = *reinterpret_cast<const uint4*>(&lds_q[r][16 * c16]);
-            st_stream<MXTILE_NT_STORE>(reinterpret_cast<uint4*>(q_row + (w0 + r) * K + kw + 16 * c16), val);
+            st_stream<MXGRP_NT_STORE>(reinterpret_cast<uint4*>(q_row + (w0 + r) * K + kw + 16 * c16), val);
         }
     }
     const int64_t nb_row = K >> 5;

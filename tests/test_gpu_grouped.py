@@ -59,6 +59,12 @@ def _cases():
     yield "whole_windows_off_grid", 8192, 512, _counts_offsets(counts)
     # the same segments over eight 256-column groups
     yield "whole_windows_off_grid_wide", 8192, 2048, _counts_offsets(counts)
+    # M % 128 == 32: the q_col rows start off line boundaries, so each window's run of a
+    # column shares its first and last line with the neighbouring windows (stored the
+    # ordinary way, the covered lines non-temporally)
+    cut = _counts_offsets(counts)
+    cut = [min(o, 8192 - 96) for o in cut]
+    yield "rows_off_line_grid_wide", 8192 - 96, 2048, cut
 
 
 CASES = list(_cases())

@@ -77,6 +77,25 @@ def test_mx_colwise_with_k_not_a_multiple_of_32(M, K):
     assert_same("dequant", bits(y), oracle.mx_dequantize(eqc, esc))
 
 
+@pytest.mark.parametrize("mode", [bsq.MX_COLWISE, bsq.MX_BOTH])
+@pytest.mark.parametrize("M,K", [(65568, 2048), (8224, 2048), (65536, 2080)])
+def test_mx_rows_or_columns_off_the_line_grid(M, K, mode):
+    """M % 128 == 32 puts every q_col row off 128-byte line boundaries (the tile's columns are
+    stored non-temporally only inside lines they cover whole); K % 128 == 32 does the same to
+    q_row.  Full-size tensors, so nearly every workgroup has such shared lines."""
+    log("mx mode %d %dx%d (off the line grid)" % (mode, M, K))
+    x = mixed_bf16(np.random.default_rng(M + 7 * K + mode), M, K)
+    qr, sr, qc, sc = _mx_gpu(x, mode)
+    eqc, esc = oracle.mx_quantize_colwise(x)
+    assert_same("q_col", qc.payload().reshape(K, M), eqc)
+    assert_same("s_col", sc.payload().reshape(K, M // 32), esc)
+    del eqc, esc
+    if mode == bsq.MX_BOTH:
+        eqr, esr = oracle.mx_quantize_rowwise(x)
+        assert_same("q_row", qr.payload().reshape(M, K), eqr)
+        assert_same("s_row", sr.payload().reshape(M, K // 32), esr)
+
+
 def test_mx_both_on_a_tensor_with_tiles_beyond_31_bit_offsets():
     """M = 2^23 + 32 rows: a workgroup tile of the columnwise copy then spans more than
     2^31 bytes of q_col, so the kernel addresses with 64-bit offsets (and the tile grid
