@@ -12,6 +12,9 @@ Two implementations live here:
   numpy arrays.  This is the oracle the parity tests compare against.
 * ``exact.py`` -- exact-rational (``fractions.Fraction``) brute-force verifier for tiny
   inputs.  It pins the C oracle; it is never timed.
+* ``numpy_ref.py`` -- a vectorized numpy re-implementation (binary32 steps as numpy
+  float32 operations) that pins the C oracle on the workloads' own tensors, where the
+  exact verifier is too slow.
 
 Every function cites the passage of the pages it follows in ``bsq_oracle.c``.
 """
