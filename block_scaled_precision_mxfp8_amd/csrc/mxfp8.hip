@@ -1104,7 +1104,10 @@ hipError_t launch_mx_quant_grouped(const void* x, int64_t M, int64_t K, int mode
 // a workgroup owns, in slot j, the 8 codes of chunk blockIdx*256*DQ_SLOTS + 256 j + t and
 // writes their 16 bytes of BF16, so every load instruction reads 512 contiguous bytes
 // and every store instruction writes 1 KiB contiguous; 4 neighbouring lanes share a scale.
-constexpr int MX_DQ_SLOTS = 2;
+#ifndef BSQ_MX_DQ_SLOTS
+#define BSQ_MX_DQ_SLOTS 2
+#endif
+constexpr int MX_DQ_SLOTS = BSQ_MX_DQ_SLOTS;
 
 __device__ __forceinline__ uint32_t fix_nan_pair(uint32_t y, uint32_t codes2) {
     const uint32_t lo = ((codes2 & 0x7Fu) == 0x7Fu) ? 0x7FC0u : (y & 0xFFFFu);

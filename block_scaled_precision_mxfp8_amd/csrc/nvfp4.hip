@@ -94,7 +94,12 @@ void nv_check_offsets_kernel(const int64_t* __restrict__ off, int64_t E, int64_t
 // rows per wave keep every lane busy and twice the bytes in flight per wave (K = 768:
 // 192 chunks fill 3 slots exactly, where one row would leave half of its second slot
 // idle).
-constexpr int NV_WAVES = 4;
+// Waves per workgroup of the row kernels (2 / 4 / 8: 449.6 / 442.5 / 439.4 us alone on
+// 524288 x 2048, but 8 slower in the step, 6159-6178 against 6179-6188 GB/s).
+#ifndef BSQ_NV_WAVES
+#define BSQ_NV_WAVES 4
+#endif
+constexpr int NV_WAVES = BSQ_NV_WAVES;
 
 // Wave index as a scalar: all address arithmetic of a span is then wave-uniform and the
 // per-lane part is a 32-bit offset.
@@ -674,7 +679,12 @@ void nv_quant_2d_kernel(const uint16_t* __restrict__ x, uint32_t* __restrict__ q
 // slot j, so loads read 256 contiguous bytes and stores write 1 KiB contiguous per
 // instruction.  The row of half block h is h / (K/8), an exact multiply-high division.
 // y = RNE_BF16(fl(exact(DEC_E2M1(q) DEC_E4M3(sb)) s_t)).
-constexpr int NV_DQ_SLOTS = 2;
+// Re-measured with the loads at raised priority: 1 / 2 / 4 slots 584 / 434 / 457 us on
+// 524288 x 2048 (the MXFP8 dequant: 71.8 / 65.4 / 68.2 us on 65536 x 2048).
+#ifndef BSQ_NV_DQ_SLOTS
+#define BSQ_NV_DQ_SLOTS 2
+#endif
+constexpr int NV_DQ_SLOTS = BSQ_NV_DQ_SLOTS;
 
 // Two BF16 (one dword) of the E2M1 codes in byte `sel` of `word`; the inner product is
 // exact, the product with s_t is one binary32 rounding, the convert is RNE to BF16.
