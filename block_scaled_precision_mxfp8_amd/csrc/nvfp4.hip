@@ -284,11 +284,19 @@ void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
 // Ordinary stores look faster for the scattered writes when the kernel is timed alone,
 // 172 -> 143 us on 65536 tokens x 2048 to top 8 of 128, but leave the dirty lines for
 // whatever runs next: timed together with the 512 MiB read that follows, 168 us with
-// non-temporal stores against 198 us with ordinary ones.
+// non-temporal stores against 198 us with ordinary ones.  A memory-only kernel with the same
+// loads and stores and no arithmetic takes 164-166 us on that workload, timed the same way.
 
 __global__ __launch_bounds__(64)
 void nv_status_clear_kernel(int32_t* __restrict__ status) {
     if (threadIdx.x == 0) *status = 0;
+}
+
+// Lane i's 64-bit value, read as a wave-uniform one.
+__device__ __forceinline__ int64_t readlane_i64(int64_t v, int i) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, i);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), i);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 template <int NS, int RPW, bool FULL>
@@ -307,6 +315,18 @@ void nv_quant_scatter_kernel(const uint4* __restrict__ h, int64_t T, int64_t K,
     const bool has_b = RPW == 2 && n_ch > cpr;
     uint4 v[NS];
     load_span<NS, FULL>(v, h + r0 * cpr, n_ch);
+    // The destination rows, 32 entries at a time, loaded together with the span: lane l < 32
+    // holds entry c0 + l of token r0, lane 32 + l the same entry of token r0 + 1 (-1 where
+    // there is none); the loop below reads them back as wave-uniform values.  Loading each
+    // entry inside the loop made every destination wait for a load and, with it, for the
+    // previous destination's stores (one counter covers both): 171.1 -> 167.5 us on 65536
+    // tokens x 2048 to 524288 Zipf-routed rows, timed with the following read.
+    const auto load_dst = [&](int64_t c0) -> int64_t {
+        const int64_t c = c0 + (lane & 31);
+        const bool second = lane >= 32;
+        return (c < top_k && (!second || has_b)) ? dst[(r0 + (second ? 1 : 0)) * top_k + c] : -1;
+    };
+    int64_t dl = load_dst(0);
     const uint32_t mm = span_amax<NS, RPW>(v, cpr);
     const float s_a = nv_decode_scale(mm & 0xFFFFu);
     const float s_b = nv_decode_scale(mm >> 16);
@@ -315,32 +335,36 @@ void nv_quant_scatter_kernel(const uint4* __restrict__ h, int64_t T, int64_t K,
     encode_span<NS, RPW>(v, cpr, s_a, s_b, packed, lsb);
     const int sbr = cpr >> 1;                         // scale bytes per row
     const bool sb16 = (sbr & 15) == 0;                // a row's scale run is whole 16-byte units
-    for (int64_t c = 0; c < top_k; ++c) {
-        const int64_t da = dst[r0 * top_k + c];
-        const int64_t db = has_b ? dst[(r0 + 1) * top_k + c] : -1;
-        const bool va = da >= 0 && da < N, vb = db >= 0 && db < N;
-        if (status != nullptr && lane == 0 && (da >= N || db >= N)) *status = 6;   // BSQ_ERR_OFFSETS
+    for (int64_t c0 = 0; c0 < top_k; c0 += 32) {
+        if (c0 > 0) dl = load_dst(c0);
+        const int n_c = (int)min<int64_t>(32, top_k - c0);
+        for (int i = 0; i < n_c; ++i) {
+            const int64_t da = readlane_i64(dl, i);
+            const int64_t db = has_b ? readlane_i64(dl, 32 + i) : -1;
+            const bool va = da >= 0 && da < N, vb = db >= 0 && db < N;
+            if (status != nullptr && lane == 0 && (da >= N || db >= N)) *status = 6;   // BSQ_ERR_OFFSETS
 #pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            const int ch = 64 * j + lane;
-            const bool inb = RPW == 2 && ch >= cpr;
-            if ((FULL || ch < n_ch) && (inb ? vb : va))
-                st_stream<NVQ_NT_STORE>(q + (inb ? db : da) * cpr + (inb ? ch - cpr : ch), packed[j]);
-        }
-        if (sb16) {
-            const int units = sbr >> 4;               // 16-byte units per row
-            const bool inb = lane >= units;
-            if (lane < (has_b ? 2 : 1) * units && (inb ? vb : va))
-                st_stream<NVQ_NT_STORE>(reinterpret_cast<uint4*>(sb + (inb ? db : da) * sbr) + (inb ? lane - units : lane),
-                                        reinterpret_cast<const uint4*>(lsb)[lane]);
-        } else {
-            for (int i = lane; i < (has_b ? 2 : 1) * sbr; i += 64) {
-                const bool inb = i >= sbr;
-                if (inb ? vb : va) sb[(inb ? db : da) * sbr + (inb ? i - sbr : i)] = lsb[i];
+            for (int j = 0; j < NS; ++j) {
+                const int ch = 64 * j + lane;
+                const bool inb = RPW == 2 && ch >= cpr;
+                if ((FULL || ch < n_ch) && (inb ? vb : va))
+                    st_stream<NVQ_NT_STORE>(q + (inb ? db : da) * cpr + (inb ? ch - cpr : ch), packed[j]);
             }
+            if (sb16) {
+                const int units = sbr >> 4;               // 16-byte units per row
+                const bool inb = lane >= units;
+                if (lane < (has_b ? 2 : 1) * units && (inb ? vb : va))
+                    st_stream<NVQ_NT_STORE>(reinterpret_cast<uint4*>(sb + (inb ? db : da) * sbr) + (inb ? lane - units : lane),
+                                            reinterpret_cast<const uint4*>(lsb)[lane]);
+            } else {
+                for (int k = lane; k < (has_b ? 2 : 1) * sbr; k += 64) {
+                    const bool inb = k >= sbr;
+                    if (inb ? vb : va) sb[(inb ? db : da) * sbr + (inb ? k - sbr : k)] = lsb[k];
+                }
+            }
+            if (lane == 0 && va) st[da] = s_a;
+            if (lane == 1 && vb) st[db] = s_b;
         }
-        if (lane == 0 && va) st[da] = s_a;
-        if (lane == 1 && vb) st[db] = s_b;
     }
 }
 
