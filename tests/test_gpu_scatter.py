@@ -43,7 +43,10 @@ def _routing(rng, T, k, drop=0.0, spare=0):
 
 CASES = [("k2048", 33, 2048, 8, 0.0, 0), ("k768_pairs_odd", 45, 768, 4, 0.0, 0),
          ("k48_dropped", 64, 48, 3, 0.25, 17), ("k8208_long", 5, 8208, 2, 0.0, 3),
-         ("k1536", 40, 1536, 8, 0.1, 0), ("k256_pairs_even", 50, 256, 6, 0.0, 0)]
+         ("k1536", 40, 1536, 8, 0.1, 0), ("k256_pairs_even", 50, 256, 6, 0.0, 0),
+         # more than 32 destinations a token: the destination rows are read in chunks of 32
+         ("k2048_top40", 9, 2048, 40, 0.1, 5), ("k768_pairs_top33", 11, 768, 33, 0.0, 0),
+         ("k512_pairs_top64", 6, 512, 64, 0.2, 1)]
 
 
 @pytest.mark.parametrize("name,T,K,k,drop,spare", CASES, ids=[c[0] for c in CASES])
