@@ -95,7 +95,8 @@ void nv_check_offsets_kernel(const int64_t* __restrict__ off, int64_t E, int64_t
 // 192 chunks fill 3 slots exactly, where one row would leave half of its second slot
 // idle).
 // Waves per workgroup of the row kernels (2 / 4 / 8: 449.6 / 442.5 / 439.4 us alone on
-// 524288 x 2048, but 8 slower in the step, 6159-6178 against 6179-6188 GB/s).
+// 524288 x 2048, but 8 slower in the step, 6159-6178 against 6179-6188 GB/s); the per-token
+// quantizer's one-row spans run one wave per workgroup instead (see launch_rows).
 #ifndef BSQ_NV_WAVES
 #define BSQ_NV_WAVES 4
 #endif
@@ -238,9 +239,9 @@ __device__ __forceinline__ void quant_span(const uint4 (&v)[NS], int64_t r0, int
     }
 }
 
-// One span per wave, per-token scales.
-template <int NS, int RPW, bool FULL>
-__global__ __launch_bounds__(64 * NV_WAVES)
+// One span per wave, WAVES waves per workgroup, per-token scales.
+template <int NS, int RPW, bool FULL, int WAVES>
+__global__ __launch_bounds__(64 * WAVES)
 void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
                           uint8_t* __restrict__ sb, float* __restrict__ st,
                           int64_t R, int64_t K,
@@ -249,9 +250,9 @@ void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
     const int wave = wave_id();
     const int lane = threadIdx.x & 63;
     if (status != nullptr && blockIdx.x == 0 && wave == 0) check_offsets(offsets, E, R, status);
-    const int64_t r0 = ((int64_t)blockIdx.x * NV_WAVES + wave) * RPW;
+    const int64_t r0 = ((int64_t)blockIdx.x * WAVES + wave) * RPW;
     if (r0 >= R) return;
-    __shared__ __align__(16) uint8_t lds_sb[NV_WAVES][32 * NS];
+    __shared__ __align__(16) uint8_t lds_sb[WAVES][32 * NS];
     const int cpr = (int)(K >> 3);                    // 8-element chunks per row
     const int n_ch = (RPW == 2 && r0 + 1 >= R) ? cpr : RPW * cpr;
     uint4 v[NS];
@@ -798,18 +799,25 @@ void nv_dequant_kernel(const uint32_t* __restrict__ q, const uint8_t* __restrict
 // ----------------------------------------------------------------------------- launch
 
 // Spans of RPW rows per wave; FULL when every span fills its NS slots exactly (the last
-// span of an odd row count under RPW = 2 takes the bounds-checked kernel).
+// span of an odd row count under RPW = 2 takes the bounds-checked kernel).  One-row spans
+// run one wave per workgroup, so that consecutive rows go to different XCDs: 450-451 ->
+// 444.5-445 us on the 524288 x 2048 routed rows inside the step (the step 6172-6186 ->
+// 6210-6219 GB/s), 168.7 -> 166.3 us on 196608 x 2048 timed with the following read; the
+// same change made two-row spans slower (262144 x 768: 82.3 -> 88.7 us), which keep
+// NV_WAVES.  Either way the grid has one wave per span, so nv_quant_launch_fits (which
+// counts NV_WAVES-wave workgroups, the stricter count) covers both.
 template <int NS, int RPW>
 static void launch_rows(const void* x, int64_t R, int64_t K, void* q, void* sb, float* st,
                         const int64_t* off, int64_t E, int32_t* status, hipStream_t stream) {
+    constexpr int WAVES = RPW == 1 ? 1 : NV_WAVES;
     const int64_t spans = (R + RPW - 1) / RPW;
-    const int64_t grid = (spans + NV_WAVES - 1) / NV_WAVES;
+    const int64_t grid = (spans + WAVES - 1) / WAVES;
     const bool full = RPW * K == 512 * NS && R % RPW == 0;
     if (full)
-        hipLaunchKernelGGL((nv_quant_rows_kernel<NS, RPW, true>), dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
+        hipLaunchKernelGGL((nv_quant_rows_kernel<NS, RPW, true, WAVES>), dim3((unsigned)grid), dim3(64 * WAVES), 0,
                            stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, st, R, K, off, E, status);
     else
-        hipLaunchKernelGGL((nv_quant_rows_kernel<NS, RPW, false>), dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
+        hipLaunchKernelGGL((nv_quant_rows_kernel<NS, RPW, false, WAVES>), dim3((unsigned)grid), dim3(64 * WAVES), 0,
                            stream, (const uint4*)x, (uint32_t*)q, (uint8_t*)sb, st, R, K, off, E, status);
 }
 
@@ -819,8 +827,10 @@ static void launch_rows(const void* x, int64_t R, int64_t K, void* q, void* sb, 
 #endif
 constexpr int64_t NV_PAIR_MAX_K = BSQ_NV_PAIR_MAX_K;
 
-// Workgroups of the per-row quantizers (per-token, grouped, per-group pass 2, scatter):
-// one wave per span of two rows up to NV_PAIR_MAX_K, of one row above.
+// Workgroups of NV_WAVES waves for the per-row quantizers (per-token, grouped, per-group
+// pass 2, scatter): one wave per span of two rows up to NV_PAIR_MAX_K, of one row above
+// (the per-token quantizer launches its one-row spans as one-wave workgroups: the same
+// waves, and a grid that fits whenever this one does).
 static int64_t nv_rows_grid(int64_t R, int64_t K) {
     const int64_t rpw = K <= NV_PAIR_MAX_K ? 2 : 1;
     return ((R + rpw - 1) / rpw + NV_WAVES - 1) / NV_WAVES;
