@@ -14,7 +14,7 @@ timed on its own with HIP events on its stream, to report its fraction of the HB
 roofline; the CPU oracle is timed on a bounded sample of the same step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--profile-pass]
+                       [--profile-pass] [--all-configs] [--profile-op OP] [--hbm-ceiling]
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -87,6 +87,10 @@ def parse():
     p.add_argument("--profile-pass", action="store_true",
                    help="short run for hardware-counter passes: one 1 GiB device copy (the "
                         "counter calibration kernel), then the steps")
+    p.add_argument("--hbm-ceiling", action="store_true",
+                   help="instead of the step: time the byte-moving probes of tests/probes "
+                        "(2 GiB read, write and copy; the NVFP4 quantizer's access pattern without "
+                        "arithmetic) next to the quantizer itself, one JSON line each")
     p.add_argument("--profile-op", choices=sorted(PROFILE_OPS),
                    help="counter pass of one extended op: one 1 GiB device copy, then the op "
                         "twice on random inputs of the benchmark's shapes")
@@ -205,6 +209,8 @@ def main():
         return all_configs(torch, bsq, workloads, dev)
     if args.profile_op:
         return profile_op(torch, bsq, workloads, dev, args.profile_op)
+    if args.hbm_ceiling:
+        return hbm_ceiling(torch, bsq, dev)
     t_gen = time.time()
     cfg = workloads.config5()
     a_np, w_np, tok, off = cfg["a"], cfg["w"], cfg["token_idx"], cfg["offsets"]
@@ -315,6 +321,92 @@ def main():
         out["cpu_baseline"] = cpu_baseline(a_np, w_np, tok, args.cpu_sample, args.cpu_reps)
 
     print(json.dumps(out), flush=True)
+
+
+def hbm_ceiling(torch, bsq, dev, reps=21):
+    """What moving the bytes costs on this device, without arithmetic: a 2 GiB read, 2 GiB
+    writes and 2 GiB -> 2 GiB copies (one 16-byte piece per lane, non-temporal loads; stores
+    non-temporal or ordinary), and the per-token NVFP4 quantizer's own access pattern on
+    524288 rows of 2048 BF16, timed beside the quantizer on the same rows; a 256 MiB copy
+    and the MXFP8 dual quantizer's access pattern beside that quantizer on the layer step's
+    65536 x 2048 activations (the copy reads and writes about as much).  Each launch
+    follows a read of a 512 MiB buffer; "alone" is the median of HIP events around the
+    launch, "with next read" times the launch together with the next 512 MiB read and
+    subtracts that read's own time, which counts write-backs a launch leaves for later."""
+    import ctypes
+    sys.path.insert(0, os.path.join(ROOT, "tests", "probes"))
+    import build_probe
+    if not os.path.exists(build_probe.HBM_LIB):
+        build_probe.build()
+    hp = ctypes.CDLL(build_probe.HBM_LIB)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    flush = torch.ones(1 << 26, dtype=torch.int64, device=dev)
+    n16 = 1 << 27                                         # 2 GiB in 16-byte pieces
+    x = torch.empty(n16 * 8, dtype=torch.int16, device=dev)
+    for c in range(8):                                    # finite BF16 bit patterns
+        part = x[c * n16:(c + 1) * n16]
+        part.copy_(torch.randint(0, 0x7F80, (n16,), dtype=torch.int32, device=dev).to(torch.int16))
+    y = torch.empty_like(x)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    R, K = 524288, 2048
+    q = torch.empty(R, K // 2, dtype=torch.uint8, device=dev)
+    sb = torch.empty(R, K // 16, dtype=torch.uint8, device=dev)
+    st = torch.empty(R, dtype=torch.float32, device=dev)
+    xb = x.view(torch.bfloat16).view(R, K)
+    MA = 65536                                            # the layer step's activations
+    a = xb[:MA]
+    a_out = (torch.empty(MA, K, dtype=torch.uint8, device=dev), torch.empty(MA, K // 32, dtype=torch.uint8, device=dev),
+             torch.empty(K, MA, dtype=torch.uint8, device=dev), torch.empty(K, MA // 32, dtype=torch.uint8, device=dev))
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def timed(fn, follow):
+        ts = []
+        for _ in range(reps):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            if follow:
+                flush.sum()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError("probe launch failed: %d" % rc)
+
+    gi = 2 * n16 * 16
+    nvb = nv_bytes(R, K)
+    probes = [
+        ("read 2 GiB", gi // 2, lambda: ok(hp.hbm_probe_read(P(x), ctypes.c_int64(n16), P(sink), sp))),
+        ("write 2 GiB, non-temporal", gi // 2, lambda: ok(hp.hbm_probe_write(P(y), ctypes.c_int64(n16), 1, sp))),
+        ("write 2 GiB, ordinary", gi // 2, lambda: ok(hp.hbm_probe_write(P(y), ctypes.c_int64(n16), 0, sp))),
+        ("copy 2 GiB, non-temporal stores", gi, lambda: ok(hp.hbm_probe_copy(P(x), P(y), ctypes.c_int64(n16), 1, sp))),
+        ("copy 2 GiB, ordinary stores", gi, lambda: ok(hp.hbm_probe_copy(P(x), P(y), ctypes.c_int64(n16), 0, sp))),
+        ("NVFP4 quantizer access pattern, 524288x2048, no arithmetic", nvb,
+         lambda: ok(hp.hbm_probe_nv_pattern(P(x), ctypes.c_int64(R), P(q), P(sb), P(st), sp))),
+        ("NVFP4 per-token quantizer (nv_quant_rows_kernel), 524288x2048", nvb,
+         lambda: bsq.nv_quantize_nvfp4_per_token(xb, q, sb, st, stream=stream)),
+        ("copy 256 MiB, non-temporal stores", 2 * (gi // 16),
+         lambda: ok(hp.hbm_probe_copy(P(x), P(y), ctypes.c_int64(n16 // 8), 1, sp))),
+        ("MXFP8 dual quantizer access pattern, 65536x2048, no arithmetic", mx_both_bytes(MA, K),
+         lambda: ok(hp.hbm_probe_mx_dual_pattern(P(a), ctypes.c_int64(MA), ctypes.c_int64(K), *map(P, a_out), sp))),
+        ("MXFP8 dual quantizer (mx_quant_tile_kernel), 65536x2048", mx_both_bytes(MA, K),
+         lambda: bsq.mx_quantize_mxfp8(a, "both", *a_out, stream=stream)),
+    ]
+    for _, _, fn in probes:                               # warm-up and launch checks
+        fn()
+    torch.cuda.synchronize()
+    t_read = timed(lambda: None, True)
+    for name, nbytes, fn in probes:
+        alone = timed(fn, False)
+        follow = timed(fn, True) - t_read
+        print(json.dumps({"probe": name, "bytes": nbytes, "alone_us": round(alone, 1),
+                          "with_next_read_us": round(follow, 1), "GB_s": round(nbytes / alone / 1e3, 1),
+                          "pct_hbm_peak": round(nbytes / alone / 1e3 / HBM_PEAK_GBS * 100, 1)}), flush=True)
 
 
 def all_configs(torch, bsq, workloads, dev, reps=21):
