@@ -464,13 +464,20 @@ void nv_group_init_kernel(uint32_t* __restrict__ amax_bits, int64_t G, const int
 #endif
 constexpr int NV_AMAX_PIECES = BSQ_NV_AMAX_PIECES;
 constexpr int64_t NV_AMAX_LDS_GROUPS = 8192;          // 32 KiB of LDS per workgroup at most
+// Up to this many groups the workgroup also keeps every group's first piece in LDS (16 KiB),
+// so the two searches of each step read LDS instead of global memory: each of their seven
+// dependent steps was a round trip to the caches, in the way of the step's loads.
+constexpr int64_t NV_AMAX_LDS_STARTS = 2048;
 
 // Group of the piece p: largest g with off[g] * cpr <= p (clamped to [0, G)); uniform.
-__device__ __forceinline__ int64_t group_of_piece(int64_t p, const int64_t* off, int64_t G, int64_t cpr) {
+// `starts` holds off[g] * cpr, in LDS or read from global memory.
+template <bool LDS_STARTS>
+__device__ __forceinline__ int64_t group_of_piece(int64_t p, const int64_t* off, const int64_t* starts,
+                                                  int64_t G, int64_t cpr) {
     int64_t lo = 0, hi = G;
     while (hi - lo > 1) {
         const int64_t mid = (lo + hi) >> 1;
-        if (off[mid] * cpr <= p) lo = mid; else hi = mid;
+        if ((LDS_STARTS ? starts[mid] : off[mid] * cpr) <= p) lo = mid; else hi = mid;
     }
     return lo;
 }
@@ -482,20 +489,27 @@ __device__ __forceinline__ void amax_put(uint32_t* table, uint32_t* amax_bits, i
     else atomicMax(amax_bits + g, m << 16);
 }
 
-template <bool LDS_TABLE>
+template <bool LDS_TABLE, bool LDS_STARTS>
 __global__ __launch_bounds__(64 * NV_WAVES)
 void nv_group_amax_kernel(const uint4* __restrict__ x, int64_t R, int64_t K,
                           const int64_t* __restrict__ off, int64_t G, uint32_t* __restrict__ amax_bits) {
-    extern __shared__ uint32_t table[];               // G entries when LDS_TABLE
+    // dynamic LDS: the G + 1 group starts (in pieces) when LDS_STARTS, then the G table
+    // entries when LDS_TABLE
+    extern __shared__ __align__(8) uint64_t lds_dyn[];
+    int64_t* starts = reinterpret_cast<int64_t*>(lds_dyn);
+    uint32_t* table = reinterpret_cast<uint32_t*>(lds_dyn + (LDS_STARTS ? G + 1 : 0));
     constexpr int64_t WAVE_PIECES = 64 * NV_AMAX_PIECES;
     const int lane = threadIdx.x & 63;
     const int64_t cpr = K >> 3;
     const int64_t n = R * cpr;
     const int64_t stride = (int64_t)gridDim.x * NV_WAVES * WAVE_PIECES;
+    if (LDS_STARTS) {
+        for (int64_t g = threadIdx.x; g <= G; g += 64 * NV_WAVES) starts[g] = off[g] * cpr;
+    }
     if (LDS_TABLE) {
         for (int64_t g = threadIdx.x; g < G; g += 64 * NV_WAVES) table[g] = 0u;
-        __syncthreads();
     }
+    if (LDS_STARTS || LDS_TABLE) __syncthreads();
     for (int64_t wb = ((int64_t)blockIdx.x * NV_WAVES + wave_id()) * WAVE_PIECES; wb < n; wb += stride) {
         const int64_t we = min(n, wb + WAVE_PIECES);
         uint32_t a[NV_AMAX_PIECES];
@@ -512,8 +526,8 @@ void nv_group_amax_kernel(const uint4* __restrict__ x, int64_t R, int64_t K,
                 a[u] = q < we ? chunk_absmax8(x[q]) : 0u;
             }
         }
-        const int64_t g0 = group_of_piece(wb, off, G, cpr);
-        const int64_t g1 = group_of_piece(we - 1, off, G, cpr);
+        const int64_t g0 = group_of_piece<LDS_STARTS>(wb, off, starts, G, cpr);
+        const int64_t g1 = group_of_piece<LDS_STARTS>(we - 1, off, starts, G, cpr);
         if (g0 == g1) {
             uint32_t m = a[0];
 #pragma unroll
@@ -521,8 +535,8 @@ void nv_group_amax_kernel(const uint4* __restrict__ x, int64_t R, int64_t K,
             amax_put<LDS_TABLE>(table, amax_bits, g0, wave_max(m), lane);
         } else {
             for (int64_t g = g0; g <= g1; ++g) {       // g1 < g0 only for invalid offsets
-                const int64_t lo = g == g0 ? wb : off[g] * cpr;
-                const int64_t hi = g == g1 ? we : off[g + 1] * cpr;
+                const int64_t lo = g == g0 ? wb : (LDS_STARTS ? starts[g] : off[g] * cpr);
+                const int64_t hi = g == g1 ? we : (LDS_STARTS ? starts[g + 1] : off[g + 1] * cpr);
                 uint32_t m = 0u;
 #pragma unroll
                 for (int u = 0; u < NV_AMAX_PIECES; ++u) {
@@ -958,11 +972,15 @@ static void launch_group_amax(const void* x, int64_t R, int64_t K, const int64_t
     const int64_t per_wg = (int64_t)NV_WAVES * 64 * NV_AMAX_PIECES;
     const int64_t need = (R * (K >> 3) + per_wg - 1) / per_wg;
     const int64_t agrid = std::min<int64_t>(need, 256 * BSQ_NV_AMAX_WGS_PER_CU);
-    if (G <= NV_AMAX_LDS_GROUPS)
-        hipLaunchKernelGGL(nv_group_amax_kernel<true>, dim3((unsigned)agrid), dim3(64 * NV_WAVES),
+    if (G <= NV_AMAX_LDS_STARTS)
+        hipLaunchKernelGGL((nv_group_amax_kernel<true, true>), dim3((unsigned)agrid), dim3(64 * NV_WAVES),
+                           (size_t)(G + 1) * sizeof(int64_t) + (size_t)G * sizeof(uint32_t), stream,
+                           (const uint4*)x, R, K, off, G, bits);
+    else if (G <= NV_AMAX_LDS_GROUPS)
+        hipLaunchKernelGGL((nv_group_amax_kernel<true, false>), dim3((unsigned)agrid), dim3(64 * NV_WAVES),
                            (size_t)G * sizeof(uint32_t), stream, (const uint4*)x, R, K, off, G, bits);
     else
-        hipLaunchKernelGGL(nv_group_amax_kernel<false>, dim3((unsigned)agrid), dim3(64 * NV_WAVES), 0, stream,
+        hipLaunchKernelGGL((nv_group_amax_kernel<false, false>), dim3((unsigned)agrid), dim3(64 * NV_WAVES), 0, stream,
                            (const uint4*)x, R, K, off, G, bits);
 }
 

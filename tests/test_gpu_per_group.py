@@ -59,13 +59,19 @@ def _many_groups():
     return ("many_groups_in_hbm", int(counts.sum()), 64, _counts_offsets(counts.tolist()))
 
 
+def _groups_beyond_lds_starts():
+    counts = np.random.default_rng(80).integers(0, 3, size=3000)
+    return ("groups_beyond_lds_starts", int(counts.sum()), 32, _counts_offsets(counts.tolist()))
+
+
 def _groups_beyond_lds_table():
     counts = np.random.default_rng(79).integers(0, 3, size=9000)
     return ("groups_beyond_lds_table", int(counts.sum()), 16, _counts_offsets(counts.tolist()))
 
 
-CASES.append(_many_groups())                                    # G > 1023: offsets searched in HBM
-CASES.append(_groups_beyond_lds_table())                        # G > 8192: maxima straight to HBM
+CASES.append(_many_groups())                  # G <= 2048: group starts and maxima table in LDS
+CASES.append(_groups_beyond_lds_starts())     # 2048 < G <= 8192: maxima table in LDS, starts read from HBM
+CASES.append(_groups_beyond_lds_table())      # G > 8192: maxima straight to HBM
 
 
 @pytest.mark.parametrize("name,R,K,off", CASES, ids=[c[0] for c in CASES])
