@@ -753,15 +753,6 @@ void nv_dequant_kernel(const uint32_t* __restrict__ q, const uint8_t* __restrict
                        const float* __restrict__ st, uint4* __restrict__ y,
                        uint32_t n_half, FastDiv halves_per_row,
                        const int64_t* __restrict__ off, int64_t G, int64_t row0) {
-    // groups of the workgroup's first and last rows (uniform searches); the threads walk
-    // from the first one only when the workgroup straddles a group boundary
-    int64_t g_first = 0, g_last = 0;
-    if (GROUPED) {
-        const uint32_t h0 = blockIdx.x * (256u * NVDQ_SLOTS);
-        const uint32_t h1 = min(h0 + 256u * NVDQ_SLOTS, n_half) - 1u;
-        g_first = group_of(row0 + fastdiv(h0, halves_per_row), off, G);
-        g_last = group_of(row0 + fastdiv(h1, halves_per_row), off, G);
-    }
     const uint32_t base = blockIdx.x * (256u * NVDQ_SLOTS) + threadIdx.x;
     uint32_t w[NVDQ_SLOTS], code[NVDQ_SLOTS];
     float s_t[NVDQ_SLOTS];
@@ -779,15 +770,26 @@ void nv_dequant_kernel(const uint32_t* __restrict__ q, const uint8_t* __restrict
         } else {
             code[j] = ok ? sb[h >> 1] : 0u;
         }
-        if (GROUPED) {
+        if (!GROUPED) s_t[j] = ok ? st[fastdiv(h, halves_per_row)] : 0.0f;
+    }
+    if (GROUPED) {
+        // groups of the workgroup's first and last rows (uniform searches, done while the
+        // codes are in flight); the threads walk from the first one only when the workgroup
+        // straddles a group boundary
+        const uint32_t h0 = blockIdx.x * (256u * NVDQ_SLOTS);
+        const uint32_t h1 = min(h0 + 256u * NVDQ_SLOTS, n_half) - 1u;
+        const int64_t g_first = group_of(row0 + fastdiv(h0, halves_per_row), off, G);
+        const int64_t g_last = group_of(row0 + fastdiv(h1, halves_per_row), off, G);
+#pragma unroll
+        for (int j = 0; j < NVDQ_SLOTS; ++j) {
+            const uint32_t h = base + 256u * j;
             int64_t g = g_first;
             if (g_last != g_first) {
                 const int64_t r = row0 + fastdiv(h, halves_per_row);
                 while (g < g_last && off[g + 1] <= r) ++g;
             }
-            s_t[j] = ok ? st[g] : 0.0f;
+            s_t[j] = h < n_half ? st[g] : 0.0f;
         }
-        else s_t[j] = ok ? st[fastdiv(h, halves_per_row)] : 0.0f;
     }
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
