@@ -1,5 +1,6 @@
 """bench.py's counter-pass mode runs every extended op it offers (the figures in the
-committed traffic summary of the extended rows come from it)."""
+committed traffic summary of the extended rows come from it), and its ceiling mode runs every
+probe (the committed ceiling summary comes from it)."""
 import json
 
 import pytest
@@ -20,4 +21,14 @@ def test_profile_op_runs(op, capsys):
     torch.cuda.synchronize()
     out = capsys.readouterr().out.strip().splitlines()
     assert json.loads(out[-1]) == {"profile_op": op}
+    torch.cuda.empty_cache()
+
+
+def test_hbm_ceiling_runs(capsys):
+    log("bench --hbm-ceiling, one timed launch per probe")
+    bench.hbm_ceiling(torch, bsq, torch.device("cuda:0"), reps=1)
+    torch.cuda.synchronize()
+    lines = [json.loads(l) for l in capsys.readouterr().out.splitlines() if l.startswith("{")]
+    assert len(lines) == 10
+    assert all(l["alone_us"] > 0 and l["bytes"] > 0 for l in lines)
     torch.cuda.empty_cache()
