@@ -59,6 +59,11 @@ def _many_groups():
     return ("many_groups_in_hbm", int(counts.sum()), 64, _counts_offsets(counts.tolist()))
 
 
+def _groups_at_lds_starts_limit():
+    counts = np.random.default_rng(81).integers(0, 3, size=2048)
+    return ("groups_at_lds_starts_limit", int(counts.sum()), 16, _counts_offsets(counts.tolist()))
+
+
 def _groups_beyond_lds_starts():
     counts = np.random.default_rng(80).integers(0, 3, size=3000)
     return ("groups_beyond_lds_starts", int(counts.sum()), 32, _counts_offsets(counts.tolist()))
@@ -70,6 +75,7 @@ def _groups_beyond_lds_table():
 
 
 CASES.append(_many_groups())                  # G <= 2048: group starts and maxima table in LDS
+CASES.append(_groups_at_lds_starts_limit())   # G == 2048, the largest LDS-staged count
 CASES.append(_groups_beyond_lds_starts())     # 2048 < G <= 8192: maxima table in LDS, starts read from HBM
 CASES.append(_groups_beyond_lds_table())      # G > 8192: maxima straight to HBM
 
