@@ -327,7 +327,8 @@ def hbm_ceiling(torch, bsq, dev, reps=21):
     """What moving the bytes costs on this device, without arithmetic: a 2 GiB read, 2 GiB
     writes and 2 GiB -> 2 GiB copies (one 16-byte piece per lane, non-temporal loads; stores
     non-temporal or ordinary), and the per-token NVFP4 quantizer's own access pattern on
-    524288 rows of 2048 BF16, timed beside the quantizer on the same rows; a 256 MiB copy
+    524288 rows of 2048 BF16, timed beside the quantizer on the same rows, and the
+    dequantizer's pattern beside the dequantizer on the quantizer's outputs; a 256 MiB copy
     and the MXFP8 dual quantizer's access pattern beside that quantizer on the layer step's
     65536 x 2048 activations (the copy reads and writes about as much).  Each launch
     follows a read of a 512 MiB buffer; "alone" is the median of HIP events around the
@@ -354,6 +355,7 @@ def hbm_ceiling(torch, bsq, dev, reps=21):
     sb = torch.empty(R, K // 16, dtype=torch.uint8, device=dev)
     st = torch.empty(R, dtype=torch.float32, device=dev)
     xb = x.view(torch.bfloat16).view(R, K)
+    yb = y.view(torch.bfloat16).view(R, K)
     MA = 65536                                            # the layer step's activations
     a = xb[:MA]
     a_out = (torch.empty(MA, K, dtype=torch.uint8, device=dev), torch.empty(MA, K // 32, dtype=torch.uint8, device=dev),
@@ -390,6 +392,11 @@ def hbm_ceiling(torch, bsq, dev, reps=21):
          lambda: ok(hp.hbm_probe_nv_pattern(P(x), ctypes.c_int64(R), P(q), P(sb), P(st), sp))),
         ("NVFP4 per-token quantizer (nv_quant_rows_kernel), 524288x2048", nvb,
          lambda: bsq.nv_quantize_nvfp4_per_token(xb, q, sb, st, stream=stream)),
+        ("NVFP4 dequantizer access pattern, 524288x2048, no arithmetic", nvb,
+         lambda: ok(hp.hbm_probe_nv_dequant_pattern(P(q), P(sb), P(st), ctypes.c_int64(R), ctypes.c_int64(K),
+                                                    P(y), sp))),
+        ("NVFP4 per-token dequantizer (nv_dequant_kernel), 524288x2048", nvb,
+         lambda: bsq.nv_dequantize(q, sb, st, yb, stream=stream)),
         ("copy 256 MiB, non-temporal stores", 2 * (gi // 16),
          lambda: ok(hp.hbm_probe_copy(P(x), P(y), ctypes.c_int64(n16 // 8), 1, sp))),
         ("MXFP8 dual quantizer access pattern, 65536x2048, no arithmetic", mx_both_bytes(MA, K),

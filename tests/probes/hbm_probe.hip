@@ -1,11 +1,12 @@
 // hbm_probe.hip -- measurement-only kernels that move bytes the way the library's kernels
 // do, with no arithmetic, so that a kernel's time can be set against what its access
 // pattern costs on the device: plain 16-byte streams (read, write, copy) and the access
-// patterns of the per-token NVFP4 quantizer on rows of 2048 BF16 and of the MXFP8 dual
-// quantizer on 128 x 256 tiles.  Not part of the library;
+// patterns of the per-token NVFP4 quantizer on rows of 2048 BF16, of its dequantizer, and of
+// the MXFP8 dual quantizer on 128 x 256 tiles.  Not part of the library;
 // `bench.py --hbm-ceiling` times them.  The streams take one 16-byte piece per lane, the
-// NVFP4 pattern one row per wave, the MXFP8 pattern one tile per workgroup (no grid-stride
-// loops); the host wrappers below size the grids and check the sizes.
+// NVFP4 quantizer pattern one row per wave, the dequantizer two output pieces a thread, the
+// MXFP8 pattern one tile per workgroup (no grid-stride loops); the host wrappers below size
+// the grids and check the sizes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -132,6 +133,33 @@ __global__ __launch_bounds__(256) void mx_dual_pattern_kernel(const uint8_t* __r
         *reinterpret_cast<const uint32_t*>(lsc[threadIdx.x]);
 }
 
+// The per-token NVFP4 dequantizer's traffic: 256 threads a workgroup, two slots a thread;
+// for half block h (8 elements) a thread loads the code dword h, scale byte h / 2 and token
+// scale h / hpr, and writes 16 bytes of output at h.  The stored dwords are a, a+1, a+2, a+3
+// for a = code ^ scale byte ^ token-scale bits, not BF16 values.
+__global__ __launch_bounds__(256) void nv_dq_pattern_kernel(const uint32_t* __restrict__ q, const uint8_t* __restrict__ sb,
+                                                            const float* __restrict__ s, u32x4* __restrict__ y,
+                                                            uint32_t n_half, uint32_t hpr) {
+    const uint32_t base = blockIdx.x * 512u + threadIdx.x;
+    uint32_t w[2], c[2], t[2];
+    __builtin_amdgcn_s_setprio(3);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t h = base + 256u * j;
+        const bool ok = h < n_half;
+        w[j] = ok ? q[h] : 0u;
+        c[j] = ok ? sb[h >> 1] : 0u;
+        t[j] = ok ? __float_as_uint(s[h / hpr]) : 0u;
+    }
+    __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t h = base + 256u * j;
+        const uint32_t a = w[j] ^ c[j] ^ t[j];
+        if (h < n_half) st<true>(y + h, u32x4{a, a + 1u, a + 2u, a + 3u});
+    }
+}
+
 bool pieces_ok(int64_t n16) { return n16 > 0 && n16 % 256 == 0 && n16 / 256 < (int64_t(1) << 31); }
 
 }  // namespace
@@ -164,6 +192,16 @@ int hbm_probe_nv_pattern(const void* x, int64_t R, void* q, void* sb, void* s, v
     if (R <= 0 || R >= (int64_t(1) << 26)) return (int)hipErrorInvalidValue;
     hipLaunchKernelGGL(nv_pattern_kernel, dim3((unsigned)R), dim3(64), 0, (hipStream_t)stream,
                        (const u32x4*)x, (uint32_t*)q, (uint8_t*)sb, (float*)s);
+    return (int)hipGetLastError();
+}
+// q: R * K / 2 bytes, sb: R * K / 16 bytes, s: R floats, y: R * K BF16; K a positive
+// multiple of 16, 0 < R * K / 8 < 2^32.
+int hbm_probe_nv_dequant_pattern(const void* q, const void* sb, const void* s, int64_t R, int64_t K, void* y,
+                                 void* stream) {
+    if (R <= 0 || K <= 0 || K % 16 != 0 || R * (K / 8) >= (int64_t(1) << 32)) return (int)hipErrorInvalidValue;
+    const uint32_t n_half = (uint32_t)(R * (K / 8));
+    hipLaunchKernelGGL(nv_dq_pattern_kernel, dim3((n_half + 511u) / 512u), dim3(256), 0, (hipStream_t)stream,
+                       (const uint32_t*)q, (const uint8_t*)sb, (const float*)s, (u32x4*)y, n_half, (uint32_t)(K / 8));
     return (int)hipGetLastError();
 }
 // x: M x K BF16; q_row M * K, s_row M * K / 32, q_col K * M, s_col K * M / 32 bytes;

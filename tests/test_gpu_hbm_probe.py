@@ -1,7 +1,8 @@
 """The byte-moving probes that `bench.py --hbm-ceiling` times (tests/probes/hbm_probe.hip)
 move the bytes they claim to: the copy reproduces its input, the write stores its pattern,
 and the two access-pattern probes write the output arrays of the quantizers they stand for
-(NVFP4 codes, block and token scales; MXFP8 rowwise and columnwise codes and scales), with
+(NVFP4 codes, block and token scales, and the dequantized rows; MXFP8 rowwise and
+columnwise codes and scales), with
 the values they are stated to write where those are simple, and nothing around them."""
 import ctypes
 import os
@@ -93,3 +94,27 @@ def test_mx_dual_pattern_probe_writes_both_copies():
     xw = x.cpu().numpy().view(np.uint32).reshape(M, K // 8, 4)
     want = np.stack([xw[..., 0] ^ xw[..., 1], xw[..., 2] ^ xw[..., 3]], axis=-1).reshape(M, K // 4)
     assert np.array_equal(views[0].cpu().numpy().view(np.uint32).reshape(M, K // 4), want)
+
+
+def test_nv_dequant_pattern_probe_writes_every_piece():
+    log("hbm probe NVFP4 dequant pattern, 33 x 2048")
+    hp = _lib()
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    R, K, pad = 33, 2048, 4096                     # 8448 half blocks: a partial last workgroup
+    q = torch.randint(-2**31, 2**31 - 1, (R * K // 8,), dtype=torch.int32, device="cuda")
+    sb = torch.randint(0, 256, (R * K // 16,), dtype=torch.uint8, device="cuda")
+    st = torch.randn(R, device="cuda")
+    y = torch.full((R * K * 2 + 2 * pad,), 0xA5, dtype=torch.uint8, device="cuda")
+    yv = y[pad:pad + R * K * 2]
+    assert hp.hbm_probe_nv_dequant_pattern(_p(q), _p(sb), _p(st), ctypes.c_int64(R), ctypes.c_int64(K),
+                                           _p(yv), s) == 0
+    assert hp.hbm_probe_nv_dequant_pattern(_p(q), _p(sb), _p(st), ctypes.c_int64(R), ctypes.c_int64(K + 8),
+                                           _p(yv), s) != 0
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    assert np.all(yh[:pad] == 0xA5) and np.all(yh[-pad:] == 0xA5)
+    h = np.arange(R * K // 8)
+    a = (q.cpu().numpy().view(np.uint32) ^ sb.cpu().numpy()[h >> 1].astype(np.uint32)
+         ^ st.cpu().numpy().view(np.uint32)[h // (K // 8)])
+    want = np.stack([a, a + 1, a + 2, a + 3], axis=1).astype(np.uint32)
+    assert np.array_equal(yv.cpu().numpy().view(np.uint32).reshape(-1, 4), want)
