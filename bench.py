@@ -327,8 +327,9 @@ def hbm_ceiling(torch, bsq, dev, reps=21):
     """What moving the bytes costs on this device, without arithmetic: a 2 GiB read, 2 GiB
     writes and 2 GiB -> 2 GiB copies (one 16-byte piece per lane, non-temporal loads; stores
     non-temporal or ordinary), and the per-token NVFP4 quantizer's own access pattern on
-    524288 rows of 2048 BF16, timed beside the quantizer on the same rows, and the
-    dequantizer's pattern beside the dequantizer on the quantizer's outputs; a 256 MiB copy
+    524288 rows of 2048 BF16, timed beside the quantizer on the same rows, the dequantizer's
+    pattern beside the dequantizer on the quantizer's outputs, and the quantize-then-scatter's
+    pattern beside it (65536 tokens to the 524288 Zipf-routed rows); a 256 MiB copy
     and the MXFP8 dual quantizer's access pattern beside that quantizer on the layer step's
     65536 x 2048 activations (the copy reads and writes about as much).  Each launch
     follows a read of a 512 MiB buffer; "alone" is the median of HIP events around the
@@ -356,6 +357,11 @@ def hbm_ceiling(torch, bsq, dev, reps=21):
     st = torch.empty(R, dtype=torch.float32, device=dev)
     xb = x.view(torch.bfloat16).view(R, K)
     yb = y.view(torch.bfloat16).view(R, K)
+    T = 65536                                             # tokens routed to 8 of 128 experts (Zipf 1.1)
+    import workloads
+    tok, _ = workloads.zipf_routing(np.random.default_rng(4), T, 128, 8)
+    dst = torch.from_numpy(workloads.scatter_rows(tok, T, 8)).to(dev)
+    scb = 2 * T * K + R * (K // 2 + K // 16 + 4) + 8 * T * 8
     MA = 65536                                            # the layer step's activations
     a = xb[:MA]
     a_out = (torch.empty(MA, K, dtype=torch.uint8, device=dev), torch.empty(MA, K // 32, dtype=torch.uint8, device=dev),
@@ -397,6 +403,13 @@ def hbm_ceiling(torch, bsq, dev, reps=21):
                                                     P(y), sp))),
         ("NVFP4 per-token dequantizer (nv_dequant_kernel), 524288x2048", nvb,
          lambda: bsq.nv_dequantize(q, sb, st, yb, stream=stream)),
+        ("quantize-then-scatter access pattern, 65536 tokens x 2048 -> 524288 rows, no arithmetic", scb,
+         lambda: ok(hp.hbm_probe_scatter_pattern(P(x), ctypes.c_int64(T), P(dst), 8, ctypes.c_int64(R),
+                                                 P(q), P(sb), P(st), sp))),
+        ("NVFP4 quantize-then-scatter (nv_quant_scatter_kernel), 65536 tokens x 2048 -> 524288 rows", scb,
+         lambda: ok(bsq.lib().nv_quantize_nvfp4_per_token_scatter(x.data_ptr(), T, K, dst.data_ptr(), 8, R,
+                                                                  q.data_ptr(), sb.data_ptr(), st.data_ptr(),
+                                                                  None, stream.cuda_stream))),
         ("copy 256 MiB, non-temporal stores", 2 * (gi // 16),
          lambda: ok(hp.hbm_probe_copy(P(x), P(y), ctypes.c_int64(n16 // 8), 1, sp))),
         ("MXFP8 dual quantizer access pattern, 65536x2048, no arithmetic", mx_both_bytes(MA, K),

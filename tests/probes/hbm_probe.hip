@@ -1,12 +1,12 @@
 // hbm_probe.hip -- measurement-only kernels that move bytes the way the library's kernels
 // do, with no arithmetic, so that a kernel's time can be set against what its access
 // pattern costs on the device: plain 16-byte streams (read, write, copy) and the access
-// patterns of the per-token NVFP4 quantizer on rows of 2048 BF16, of its dequantizer, and of
-// the MXFP8 dual quantizer on 128 x 256 tiles.  Not part of the library;
-// `bench.py --hbm-ceiling` times them.  The streams take one 16-byte piece per lane, the
+// patterns of the per-token NVFP4 quantizer on rows of 2048 BF16, of its dequantizer, of the
+// quantize-then-scatter, and of the MXFP8 dual quantizer on 128 x 256 tiles.  Not part of
+// the library; `bench.py --hbm-ceiling` times them.  The streams take one 16-byte piece per lane, the
 // NVFP4 quantizer pattern one row per wave, the dequantizer two output pieces a thread, the
-// MXFP8 pattern one tile per workgroup (no grid-stride loops); the host wrappers below size
-// the grids and check the sizes.
+// scatter one token per wave, the MXFP8 pattern one tile per workgroup (no grid-stride
+// loops); the host wrappers below size the grids and check the sizes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -160,6 +160,49 @@ __global__ __launch_bounds__(256) void nv_dq_pattern_kernel(const uint32_t* __re
     }
 }
 
+// The quantize-then-scatter's traffic on tokens of 2048 BF16: one wave per token and per
+// workgroup reads the token (four 16-byte loads a lane at raised priority) and its
+// destination rows (one load, entries 0..top_k-1 in lanes 0..top_k-1, top_k <= 64), then for
+// each destination writes the row's 1 KiB of codes as 4-byte stores, its 128 scale bytes
+// (eight 16-byte stores, gathered in LDS) and its 4-byte token scale.  Values are XORs of
+// the loaded ones.  Entries outside [0, N) are skipped.
+__global__ __launch_bounds__(64) void scatter_pattern_kernel(const u32x4* __restrict__ x, const int64_t* __restrict__ dst,
+                                                             int top_k, int64_t N, uint32_t* __restrict__ q,
+                                                             uint8_t* __restrict__ sb, float* __restrict__ s) {
+    __shared__ __align__(16) uint8_t lsb[128];
+    const int lane = threadIdx.x & 63;
+    const int64_t t = blockIdx.x;
+    const u32x4* xr = x + t * 256;
+    u32x4 v[4];
+    __builtin_amdgcn_s_setprio(3);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = ld_nt(xr + 64 * j + lane);
+    __builtin_amdgcn_s_setprio(0);
+    const int64_t dl = lane < top_k ? dst[t * top_k + lane] : -1;
+    uint32_t p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j] = v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    if ((lane & 1) == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lsb[32 * j + (lane >> 1)] = (uint8_t)v[j].x;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const u32x4 sv = reinterpret_cast<const u32x4*>(lsb)[lane & 7];
+    for (int i = 0; i < top_k; ++i) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)dl, i);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)dl >> 32), i);
+        const int64_t d = (int64_t)(((uint64_t)hi << 32) | lo);
+        if (d < 0 || d >= N) continue;
+        uint32_t* qr = q + d * 256;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(p[j], qr + 64 * j + lane);
+        if (lane < 8) __builtin_nontemporal_store(sv, reinterpret_cast<u32x4*>(sb + d * 128) + lane);
+        if (lane == 0) s[d] = __uint_as_float(p[0]);
+    }
+}
+
 bool pieces_ok(int64_t n16) { return n16 > 0 && n16 % 256 == 0 && n16 / 256 < (int64_t(1) << 31); }
 
 }  // namespace
@@ -192,6 +235,15 @@ int hbm_probe_nv_pattern(const void* x, int64_t R, void* q, void* sb, void* s, v
     if (R <= 0 || R >= (int64_t(1) << 26)) return (int)hipErrorInvalidValue;
     hipLaunchKernelGGL(nv_pattern_kernel, dim3((unsigned)R), dim3(64), 0, (hipStream_t)stream,
                        (const u32x4*)x, (uint32_t*)q, (uint8_t*)sb, (float*)s);
+    return (int)hipGetLastError();
+}
+// x: T tokens of 2048 BF16; dst: int64 [T][top_k], 1 <= top_k <= 64; q: N * 1024 bytes,
+// sb: N * 128 bytes, s: N floats; 0 < T < 2^31.
+int hbm_probe_scatter_pattern(const void* x, int64_t T, const int64_t* dst, int top_k, int64_t N, void* q,
+                              void* sb, void* s, void* stream) {
+    if (T <= 0 || T >= (int64_t(1) << 31) || top_k < 1 || top_k > 64 || N < 0) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(scatter_pattern_kernel, dim3((unsigned)T), dim3(64), 0, (hipStream_t)stream,
+                       (const u32x4*)x, dst, top_k, N, (uint32_t*)q, (uint8_t*)sb, (float*)s);
     return (int)hipGetLastError();
 }
 // q: R * K / 2 bytes, sb: R * K / 16 bytes, s: R floats, y: R * K BF16; K a positive

@@ -1,8 +1,8 @@
 """The byte-moving probes that `bench.py --hbm-ceiling` times (tests/probes/hbm_probe.hip)
 move the bytes they claim to: the copy reproduces its input, the write stores its pattern,
 and the two access-pattern probes write the output arrays of the quantizers they stand for
-(NVFP4 codes, block and token scales, and the dequantized rows; MXFP8 rowwise and
-columnwise codes and scales), with
+(NVFP4 codes, block and token scales, the dequantized rows and the routed rows of the
+scatter; MXFP8 rowwise and columnwise codes and scales), with
 the values they are stated to write where those are simple, and nothing around them."""
 import ctypes
 import os
@@ -118,3 +118,36 @@ def test_nv_dequant_pattern_probe_writes_every_piece():
          ^ st.cpu().numpy().view(np.uint32)[h // (K // 8)])
     want = np.stack([a, a + 1, a + 2, a + 3], axis=1).astype(np.uint32)
     assert np.array_equal(yv.cpu().numpy().view(np.uint32).reshape(-1, 4), want)
+
+
+def test_scatter_pattern_probe_writes_only_named_rows():
+    log("hbm probe scatter pattern, 40 tokens x 2048, top 3 of 130 rows")
+    hp = _lib()
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    T, K, k, N = 40, 2048, 3, 130
+    rng = np.random.default_rng(5)
+    dst_np = rng.permutation(N)[:T * k].reshape(T, k).astype(np.int64)
+    dst_np[0, 1] = -1                                    # a dropped choice
+    dst_np[1, 2] = N + 3                                 # outside the rows: skipped
+    written = np.zeros(N, bool)
+    written[dst_np[(dst_np >= 0) & (dst_np < N)]] = True
+    x = torch.randint(0, 0x7F80, (T * K,), dtype=torch.int32, device="cuda").to(torch.int16)
+    dst = torch.from_numpy(dst_np).cuda()
+    q = torch.full((N * K // 2,), 0xA5, dtype=torch.uint8, device="cuda")
+    sb = torch.full((N * K // 16,), 0xA5, dtype=torch.uint8, device="cuda")
+    st = torch.full((N,), -7.0, dtype=torch.float32, device="cuda")
+    assert hp.hbm_probe_scatter_pattern(_p(x), ctypes.c_int64(T), _p(dst), k, ctypes.c_int64(N),
+                                        _p(q), _p(sb), _p(st), s) == 0
+    assert hp.hbm_probe_scatter_pattern(_p(x), ctypes.c_int64(T), _p(dst), 65, ctypes.c_int64(N),
+                                        _p(q), _p(sb), _p(st), s) != 0
+    torch.cuda.synchronize()
+    qh = q.cpu().numpy().reshape(N, K // 2)
+    assert np.all(qh[~written] == 0xA5) and np.all(sb.cpu().numpy().reshape(N, K // 16)[~written] == 0xA5)
+    assert np.all(st.cpu().numpy()[~written] == -7.0)
+    # each named row holds its token's codes: the XOR of each lane's four loaded dwords
+    xw = x.cpu().numpy().view(np.uint32).reshape(T, 256, 4)
+    want = np.bitwise_xor.reduce(xw, axis=2).astype(np.uint32)
+    for t in range(T):
+        for d in dst_np[t]:
+            if 0 <= d < N:
+                assert np.array_equal(qh[d].view(np.uint32), want[t])
