@@ -260,7 +260,7 @@ void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
     // get their reads out ahead of the others' arithmetic and stores: 458 -> 447 us on
     // 524288 x 2048; with the same in the dequantizers and the MXFP8 tile kernel, the step
     // 6123 -> 6191 GB/s (means of three interleaved runs).  (Measured and not kept, as
-    // slower: the same in the quantize-then-scatter, +3%, and the 16x16-tile quantizer.)
+    // slower: the same in the 16x16-tile quantizer.)
     __builtin_amdgcn_s_setprio(3);
     load_span<NS, FULL>(v, x + r0 * cpr, n_ch);
     __builtin_amdgcn_s_setprio(0);
@@ -300,22 +300,30 @@ __device__ __forceinline__ int64_t readlane_i64(int64_t v, int i) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-template <int NS, int RPW, bool FULL>
-__global__ __launch_bounds__(64 * NV_WAVES)
+template <int NS, int RPW, bool FULL, int WAVES>
+__global__ __launch_bounds__(64 * WAVES)
 void nv_quant_scatter_kernel(const uint4* __restrict__ h, int64_t T, int64_t K,
                              const int64_t* __restrict__ dst, int64_t top_k, int64_t N,
                              uint32_t* __restrict__ q, uint8_t* __restrict__ sb, float* __restrict__ st,
                              int32_t* __restrict__ status) {
     const int wave = wave_id();
     const int lane = threadIdx.x & 63;
-    const int64_t r0 = ((int64_t)blockIdx.x * NV_WAVES + wave) * RPW;
+    const int64_t r0 = ((int64_t)blockIdx.x * WAVES + wave) * RPW;
     if (r0 >= T) return;
-    __shared__ __align__(16) uint8_t lds_sb[NV_WAVES][32 * NS];
+    __shared__ __align__(16) uint8_t lds_sb[WAVES][32 * NS];
     const int cpr = (int)(K >> 3);
     const int n_ch = (RPW == 2 && r0 + 1 >= T) ? cpr : RPW * cpr;
     const bool has_b = RPW == 2 && n_ch > cpr;
     uint4 v[NS];
+    // Single-row spans (one wave per workgroup) load at raised priority, as in the row
+    // kernel: the two together 166.1 -> 158.8 us on 65536 tokens x 2048 to 524288
+    // Zipf-routed rows (174.1 -> 165.4 us on a random map), timed with the following read,
+    // where one wave per workgroup alone measured 166.7 us and the priority alone, with
+    // four waves per workgroup, 173.8.  Two-row spans keep four waves and ordinary
+    // priority (with it 131072 tokens x 768: 173.2 -> 177.3 us).
+    if (RPW == 1) __builtin_amdgcn_s_setprio(3);
     load_span<NS, FULL>(v, h + r0 * cpr, n_ch);
+    if (RPW == 1) __builtin_amdgcn_s_setprio(0);
     // The destination rows, 32 entries at a time, loaded together with the span: lane l < 32
     // holds entry c0 + l of token r0, lane 32 + l the same entry of token r0 + 1 (-1 where
     // there is none); the loop below reads them back as wave-uniform values.  Loading each
@@ -845,8 +853,8 @@ constexpr int64_t NV_PAIR_MAX_K = BSQ_NV_PAIR_MAX_K;
 
 // Workgroups of NV_WAVES waves for the per-row quantizers (per-token, grouped, per-group
 // pass 2, scatter): one wave per span of two rows up to NV_PAIR_MAX_K, of one row above
-// (the per-token quantizer launches its one-row spans as one-wave workgroups: the same
-// waves, and a grid that fits whenever this one does).
+// (the per-token quantizer and the scatter launch their one-row spans as one-wave
+// workgroups: the same waves, and a grid that fits whenever this one does).
 static int64_t nv_rows_grid(int64_t R, int64_t K) {
     const int64_t rpw = K <= NV_PAIR_MAX_K ? 2 : 1;
     return ((R + rpw - 1) / rpw + NV_WAVES - 1) / NV_WAVES;
@@ -1061,15 +1069,17 @@ hipError_t launch_nv_quant_group(const void* x, int64_t R, int64_t K, const int6
 template <int NS, int RPW>
 static void launch_scatter(const void* h, int64_t T, int64_t K, const int64_t* dst, int64_t top_k, int64_t N,
                            void* q, void* sb, float* st, int32_t* status, hipStream_t stream) {
+    // One wave per workgroup for single-row spans, as in the row kernel.
+    constexpr int WAVES = RPW == 1 ? 1 : NV_WAVES;
     const int64_t spans = (T + RPW - 1) / RPW;
-    const int64_t grid = (spans + NV_WAVES - 1) / NV_WAVES;
+    const int64_t grid = (spans + WAVES - 1) / WAVES;
     const bool full = RPW * K == 512 * NS && T % RPW == 0;
     if (full)
-        hipLaunchKernelGGL((nv_quant_scatter_kernel<NS, RPW, true>), dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
-                           stream, (const uint4*)h, T, K, dst, top_k, N, (uint32_t*)q, (uint8_t*)sb, st, status);
+        hipLaunchKernelGGL((nv_quant_scatter_kernel<NS, RPW, true, WAVES>), dim3((unsigned)grid), dim3(64 * WAVES),
+                           0, stream, (const uint4*)h, T, K, dst, top_k, N, (uint32_t*)q, (uint8_t*)sb, st, status);
     else
-        hipLaunchKernelGGL((nv_quant_scatter_kernel<NS, RPW, false>), dim3((unsigned)grid), dim3(64 * NV_WAVES), 0,
-                           stream, (const uint4*)h, T, K, dst, top_k, N, (uint32_t*)q, (uint8_t*)sb, st, status);
+        hipLaunchKernelGGL((nv_quant_scatter_kernel<NS, RPW, false, WAVES>), dim3((unsigned)grid), dim3(64 * WAVES),
+                           0, stream, (const uint4*)h, T, K, dst, top_k, N, (uint32_t*)q, (uint8_t*)sb, st, status);
 }
 
 hipError_t launch_nv_quant_scatter(const void* h, int64_t T, int64_t K, const int64_t* dst, int64_t top_k,
