@@ -331,7 +331,8 @@ def hbm_ceiling(torch, bsq, dev, reps=21):
     pattern beside the dequantizer on the quantizer's outputs, and the quantize-then-scatter's
     pattern beside it (65536 tokens to the 524288 Zipf-routed rows); a 256 MiB copy
     and the MXFP8 dual quantizer's access pattern beside that quantizer on the layer step's
-    65536 x 2048 activations (the copy reads and writes about as much).  Each launch
+    65536 x 2048 activations, and a 24 MiB copy with the same pattern and quantizer on its
+    2048 x 6144 weights (each copy reads and writes about as much).  Each launch
     follows a read of a 512 MiB buffer; "alone" is the median of HIP events around the
     launch, "with next read" times the launch together with the next 512 MiB read and
     subtracts that read's own time, which counts write-backs a launch leaves for later."""
@@ -366,6 +367,10 @@ def hbm_ceiling(torch, bsq, dev, reps=21):
     a = xb[:MA]
     a_out = (torch.empty(MA, K, dtype=torch.uint8, device=dev), torch.empty(MA, K // 32, dtype=torch.uint8, device=dev),
              torch.empty(K, MA, dtype=torch.uint8, device=dev), torch.empty(K, MA // 32, dtype=torch.uint8, device=dev))
+    MW, KW = 2048, 6144                                   # the layer step's weights
+    w = x.view(torch.bfloat16)[:MW * KW].view(MW, KW)
+    w_out = (torch.empty(MW, KW, dtype=torch.uint8, device=dev), torch.empty(MW, KW // 32, dtype=torch.uint8, device=dev),
+             torch.empty(KW, MW, dtype=torch.uint8, device=dev), torch.empty(KW, MW // 32, dtype=torch.uint8, device=dev))
     P = lambda t: ctypes.c_void_p(t.data_ptr())
 
     def timed(fn, follow):
@@ -416,6 +421,12 @@ def hbm_ceiling(torch, bsq, dev, reps=21):
          lambda: ok(hp.hbm_probe_mx_dual_pattern(P(a), ctypes.c_int64(MA), ctypes.c_int64(K), *map(P, a_out), sp))),
         ("MXFP8 dual quantizer (mx_quant_tile_kernel), 65536x2048", mx_both_bytes(MA, K),
          lambda: bsq.mx_quantize_mxfp8(a, "both", *a_out, stream=stream)),
+        ("copy 24 MiB, non-temporal stores", 4 * MW * KW,
+         lambda: ok(hp.hbm_probe_copy(P(x), P(y), ctypes.c_int64(2 * MW * KW // 16), 1, sp))),
+        ("MXFP8 dual quantizer access pattern, 2048x6144, no arithmetic", mx_both_bytes(MW, KW),
+         lambda: ok(hp.hbm_probe_mx_dual_pattern(P(w), ctypes.c_int64(MW), ctypes.c_int64(KW), *map(P, w_out), sp))),
+        ("MXFP8 dual quantizer (mx_quant_tile_kernel), 2048x6144", mx_both_bytes(MW, KW),
+         lambda: bsq.mx_quantize_mxfp8(w, "both", *w_out, stream=stream)),
     ]
     for _, _, fn in probes:                               # warm-up and launch checks
         fn()

@@ -29,6 +29,6 @@ def test_hbm_ceiling_runs(capsys):
     bench.hbm_ceiling(torch, bsq, torch.device("cuda:0"), reps=1)
     torch.cuda.synchronize()
     lines = [json.loads(l) for l in capsys.readouterr().out.splitlines() if l.startswith("{")]
-    assert len(lines) == 14
+    assert len(lines) == 17
     assert all(l["alone_us"] > 0 and l["bytes"] > 0 for l in lines)
     torch.cuda.empty_cache()
