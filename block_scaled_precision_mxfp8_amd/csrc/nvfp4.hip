@@ -96,7 +96,8 @@ void nv_check_offsets_kernel(const int64_t* __restrict__ off, int64_t E, int64_t
 // idle).
 // Waves per workgroup of the row kernels (2 / 4 / 8: 449.6 / 442.5 / 439.4 us alone on
 // 524288 x 2048, but 8 slower in the step, 6159-6178 against 6179-6188 GB/s); the per-token
-// quantizer's one-row spans run one wave per workgroup instead (see launch_rows).
+// quantizer's and the scatter's one-row spans run one wave per workgroup instead (see
+// launch_rows and launch_scatter).
 #ifndef BSQ_NV_WAVES
 #define BSQ_NV_WAVES 4
 #endif
@@ -285,8 +286,9 @@ void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
 // Ordinary stores look faster for the scattered writes when the kernel is timed alone,
 // 172 -> 143 us on 65536 tokens x 2048 to top 8 of 128, but leave the dirty lines for
 // whatever runs next: timed together with the 512 MiB read that follows, 168 us with
-// non-temporal stores against 198 us with ordinary ones.  A memory-only kernel with the same
-// loads and stores and no arithmetic takes 164-166 us on that workload, timed the same way.
+// non-temporal stores against 198 us with ordinary ones (since then 159 us, with the launch
+// shape below).  A memory-only kernel with the same loads and stores and no arithmetic,
+// launched the same way, takes as long (156 us kernel-only on that workload).
 
 __global__ __launch_bounds__(64)
 void nv_status_clear_kernel(int32_t* __restrict__ status) {
