@@ -89,8 +89,9 @@ def parse():
                         "counter calibration kernel), then the steps")
     p.add_argument("--hbm-ceiling", action="store_true",
                    help="instead of the step: time the byte-moving probes of tests/probes "
-                        "(2 GiB read, write and copy; the NVFP4 quantizer's access pattern without "
-                        "arithmetic) next to the quantizer itself, one JSON line each")
+                        "(read, write and copy; memory-only copies of the access patterns of the "
+                        "NVFP4 quantizer and dequantizer, the quantize-then-scatter and the MXFP8 "
+                        "dual quantizer) next to the kernels themselves, one JSON line each")
     p.add_argument("--profile-op", choices=sorted(PROFILE_OPS),
                    help="counter pass of one extended op: one 1 GiB device copy, then the op "
                         "twice on random inputs of the benchmark's shapes")

@@ -17,10 +17,10 @@ def _bf16(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-GROUPED_S_COL = 10                                         # index of the grouped s_col in _work's list
+GROUPED_S_COL = 10                                         # index of the grouped s_col in _run_all's list
 
 
-def _work(x, off, stream):
+def _run_all(x, off, stream):
     """One call of every kind on x; returns the outputs as uint8 tensors."""
     outs = []
     outs += bsq.mx_quantize_mxfp8(x, "both", stream=stream)
@@ -43,7 +43,7 @@ def test_concurrent_host_threads_match_sequential_calls():
         off = torch.from_numpy(np.concatenate([[0], cuts, [M]]).astype(np.int64)).cuda()
         inputs.append((_bf16(mixed_bf16(rng, M, K)), off))
     main = torch.cuda.current_stream()
-    expected = [[t.clone() for t in _work(x, off, main)] for x, off in inputs]
+    expected = [[t.clone() for t in _run_all(x, off, main)] for x, off in inputs]
     torch.cuda.synchronize()
 
     results, errors = [None] * n_threads, []
@@ -54,7 +54,7 @@ def test_concurrent_host_threads_match_sequential_calls():
             x, off = inputs[i]
             with torch.cuda.stream(s):
                 for _ in range(reps):
-                    got = _work(x, off, s)
+                    got = _run_all(x, off, s)
             s.synchronize()
             results[i] = got
         except Exception as e:            # reported by the main thread
