@@ -77,7 +77,8 @@ def main(argv) -> int:
     build_library()
     logs = tempfile.mkdtemp(prefix="bsq_san_")
     env = dict(os.environ)
-    env["LD_PRELOAD"] = asan_runtime()
+    # the ASan runtime must come first; an LD_PRELOAD already set stays after it
+    env["LD_PRELOAD"] = " ".join(x for x in (asan_runtime(), os.environ.get("LD_PRELOAD", "")) if x)
     # reports go to files: pytest captures the test's stderr, which an abort would lose
     env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1:log_path=%s/asan" % logs
     env["UBSAN_OPTIONS"] = "print_stacktrace=1:halt_on_error=1:log_path=%s/ubsan" % logs

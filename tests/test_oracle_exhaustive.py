@@ -9,6 +9,7 @@ import os
 import subprocess
 
 import oracle
+from host_env import child_env
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -21,7 +22,7 @@ def test_encoders_agree_on_every_binary32_value(tmp_path):
     subprocess.run(["gcc", "-O2", "-fopenmp", "-Wall", "-Wextra", "-Werror", os.path.join(HERE, "exhaustive", "enc_sweep.c"),
                     "-L" + os.path.dirname(lib), "-l:" + os.path.basename(lib),
                     "-Wl,-rpath," + os.path.dirname(lib), "-o", exe], check=True)
-    env = {k: v for k, v in os.environ.items() if k != "LD_PRELOAD"}
+    env = child_env()
     r = subprocess.run([exe], capture_output=True, text=True, timeout=600, env=env)
     print(r.stdout)
     assert r.returncode == 0, r.stdout + r.stderr
