@@ -1,0 +1,126 @@
+"""GPU parity on a tensor past 2^31 elements: 1081349 x 2048 BF16 (4.4 GB), quantized to
+per-token NVFP4 and to rowwise MXFP8 at full size on the GPU and dequantized again, then
+compared with the oracle on sampled rows.  Both formats are row-local (page "Towards
+Blackwell-native 8-bit and 4-bit RL", sections "Format background" and "Per-token activation
+scaling": a row's codes and scales depend on that row only), so the oracle's result on a
+subset of the rows is that subset of its result on the whole tensor.  The sampled rows lie
+at the start, on both sides of element 2^31 (row 2^20), at seeded random places and in the
+last rows; element and byte offsets there need more than 31 bits.  Outputs carry guard
+bytes on both sides, checked on the device."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_mxfp8_amd as bsq
+import oracle
+from gpu_helpers import GUARD, SENTINEL, assert_same, bits, log
+
+pytestmark = pytest.mark.gpu
+
+R, K = (1 << 20) + (1 << 15) + 5, 2048
+ROWS = np.unique(np.concatenate([np.arange(4), np.arange((1 << 20) - 3, (1 << 20) + 3),
+                                 np.random.default_rng(31).integers(0, R, 24), np.arange(R - 5, R)]))
+
+
+def _input():
+    """Normal values times a per-row power of two in [2^-20, 2^19], drawn on the GPU in
+    chunks (seeded), rounded to BF16: a wide spread of token scales and every element code."""
+    g = torch.Generator(device="cuda").manual_seed(2 ** 31 + 1)
+    x = torch.empty(R, K, dtype=torch.bfloat16, device="cuda")
+    step = 1 << 17
+    for a in range(0, R, step):
+        b = min(a + step, R)
+        e = torch.randint(-20, 20, (b - a, 1), generator=g, device="cuda").float()
+        x[a:b] = (torch.randn(b - a, K, generator=g, device="cuda") * torch.exp2(e)).to(torch.bfloat16)
+    return x
+
+
+def _guarded(n):
+    return torch.full((n + 2 * GUARD,), SENTINEL, dtype=torch.uint8, device="cuda")
+
+
+def _guards_intact(buf):
+    return bool((buf[:GUARD] == SENTINEL).all()) and bool((buf[-GUARD:] == SENTINEL).all())
+
+
+def _rows(t2d):
+    return bits(t2d[torch.from_numpy(ROWS).cuda()])
+
+
+@pytest.fixture(scope="module")
+def big():
+    x = _input()
+    xs = _rows(x)
+    yield x, xs
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_nv_per_token_past_2_pow_31_elements(big):
+    x, xs = big
+    log("nv per-token + dequant %dx%d (%d elements)" % (R, K, R * K))
+    assert R * K > 2 ** 31
+    qb, sbb, stb = _guarded(R * K // 2), _guarded(R * K // 16), _guarded(4 * R)
+    q = qb[GUARD:GUARD + R * K // 2].view(R, K // 2)
+    sb = sbb[GUARD:GUARD + R * K // 16].view(R, K // 16)
+    st = stb[GUARD:GUARD + 4 * R].view(torch.float32)
+    bsq.nv_quantize_nvfp4_per_token(x, q, sb, st)
+    y = bsq.nv_dequantize(q, sb, st)
+    torch.cuda.synchronize()
+    assert all(_guards_intact(b) for b in (qb, sbb, stb))
+    eq, esb, est = oracle.nv_quantize_per_token(xs)
+    assert_same("st", _rows(st.view(R, 1)).reshape(-1), est.view(np.uint32))
+    assert_same("sb", _rows(sb), esb)
+    assert_same("q", _rows(q), eq)
+    assert_same("dequant", _rows(y), oracle.nv_dequantize(eq, esb, est))
+    del q, sb, st, qb, sbb, stb, y
+    torch.cuda.empty_cache()
+
+
+def test_mx_rowwise_past_2_pow_31_elements(big):
+    x, xs = big
+    log("mx rowwise + dequant %dx%d (%d elements)" % (R, K, R * K))
+    qb, sb_ = _guarded(R * K), _guarded(R * K // 32)
+    q = qb[GUARD:GUARD + R * K].view(R, K)
+    s = sb_[GUARD:GUARD + R * K // 32].view(R, K // 32)
+    bsq.mx_quantize_mxfp8(x, "rowwise", q, s)
+    y = bsq.mx_dequantize(q, s)
+    torch.cuda.synchronize()
+    assert _guards_intact(qb) and _guards_intact(sb_)
+    eq, es = oracle.mx_quantize_rowwise(xs)
+    assert_same("s_row", _rows(s), es)
+    assert_same("q_row", _rows(q), eq)
+    assert_same("dequant", _rows(y), oracle.mx_dequantize(eq, es))
+    del q, s, qb, sb_, y
+    torch.cuda.empty_cache()
+
+
+def test_scatter_to_routed_rows_past_2_pow_31_elements(big):
+    """Quantize-then-scatter (page "Towards Blackwell-native 8-bit and 4-bit RL", section
+    "Per-token activation scaling": a token's bytes do not depend on the other rows) of the
+    first T = 2^17 + 3 rows as tokens to 8 distinct routed rows each among all R rows, in a
+    seeded random order; rows that no entry names keep their sentinel bytes."""
+    x, _ = big
+    T, k = (1 << 17) + 3, 8
+    log("nv scatter %d tokens x %d -> %d routed rows" % (T, K, R))
+    dst_np = np.random.default_rng(37).permutation(R)[:T * k].reshape(T, k).astype(np.int64)
+    src = np.full(R, -1, np.int64)                   # routed row -> token
+    src[dst_np.reshape(-1)] = np.repeat(np.arange(T), k)
+    unnamed = np.flatnonzero(src < 0)
+    q = torch.full((R, K // 2), SENTINEL, dtype=torch.uint8, device="cuda")
+    sb = torch.full((R, K // 16), SENTINEL, dtype=torch.uint8, device="cuda")
+    st = torch.full((R,), -7.0, dtype=torch.float32, device="cuda")
+    q, sb, st, status = bsq.nv_quantize_nvfp4_per_token_scatter(x[:T], torch.from_numpy(dst_np).cuda(), R, q, sb, st)
+    torch.cuda.synchronize()
+    assert int(status.item()) == bsq.BSQ_OK
+    named = ROWS[src[ROWS] >= 0]
+    assert named.size > 20 and named.max() >= (1 << 20)
+    eq, esb, est = oracle.nv_quantize_per_token(bits(x[torch.from_numpy(src[named]).cuda()]))
+    idx = torch.from_numpy(named).cuda()
+    assert_same("st", bits(st[idx]), est.view(np.uint32))
+    assert_same("sb", bits(sb[idx]), esb)
+    assert_same("q", bits(q[idx]), eq)
+    u = torch.from_numpy(unnamed[np.random.default_rng(41).integers(0, unnamed.size, 64)]).cuda()
+    assert bool((q[u] == SENTINEL).all()) and bool((sb[u] == SENTINEL).all()) and bool((st[u] == -7.0).all())
+    del q, sb, st
+    torch.cuda.empty_cache()
