@@ -1,6 +1,7 @@
 """GPU parity on a tensor past 2^31 elements: 1081349 x 2048 BF16 (4.4 GB), quantized to
-per-token NVFP4 and to rowwise MXFP8 at full size on the GPU and dequantized again, then
-compared with the oracle on sampled rows.  Both formats are row-local (page "Towards
+per-token NVFP4, to rowwise and to both MXFP8 copies at full size on the GPU and dequantized
+again, and scattered as tokens to routed rows, then compared with the oracle on sampled rows
+(and sampled 32-row blocks of the columnwise copy).  Both formats are row-local (page "Towards
 Blackwell-native 8-bit and 4-bit RL", sections "Format background" and "Per-token activation
 scaling": a row's codes and scales depend on that row only), so the oracle's result on a
 subset of the rows is that subset of its result on the whole tensor.  The sampled rows lie
@@ -123,4 +124,33 @@ def test_scatter_to_routed_rows_past_2_pow_31_elements(big):
     u = torch.from_numpy(unnamed[np.random.default_rng(41).integers(0, unnamed.size, 64)]).cuda()
     assert bool((q[u] == SENTINEL).all()) and bool((sb[u] == SENTINEL).all()) and bool((st[u] == -7.0).all())
     del q, sb, st
+    torch.cuda.empty_cache()
+
+
+def test_mx_both_past_2_pow_31_elements(big):
+    """Both MXFP8 copies of the first M = 2^20 + 96 rows (the tile grid ragged in rows): the
+    rowwise copy on the sampled rows, the columnwise copy on sampled 32-row blocks (a 32x1
+    block depends only on its own 32 rows of one column; page "Towards Blackwell-native 8-bit
+    and 4-bit RL", section "Recipe 1: end-to-end MXFP8 RL"), each dequantized as well."""
+    x, _ = big
+    M = (1 << 20) + 96
+    log("mx both + dequant %dx%d (%d elements)" % (M, K, M * K))
+    xm = x[:M]
+    q_row, s_row, q_col, s_col = bsq.mx_quantize_mxfp8(xm, "both")
+    y_col = bsq.mx_dequantize(q_col, s_col)
+    torch.cuda.synchronize()
+    rows = ROWS[ROWS < M]
+    eq, es = oracle.mx_quantize_rowwise(bits(xm[torch.from_numpy(rows).cuda()]))
+    assert_same("q_row", bits(q_row[torch.from_numpy(rows).cuda()]), eq)
+    assert_same("s_row", bits(s_row[torch.from_numpy(rows).cuda()]), es)
+    nb = M // 32
+    blocks = np.unique(np.concatenate([[0, 1, (1 << 15) - 1, 1 << 15, (1 << 15) + 1, nb - 2, nb - 1],
+                                       np.random.default_rng(43).integers(0, nb, 8)]))
+    brows = (32 * blocks[:, None] + np.arange(32)[None, :]).reshape(-1)
+    ec, esc = oracle.mx_quantize_colwise(bits(xm[torch.from_numpy(brows).cuda()]))   # [K][32 nb'], [K][nb']
+    bi, bb = torch.from_numpy(brows).cuda(), torch.from_numpy(blocks).cuda()
+    assert_same("q_col", bits(q_col[:, bi]), ec)
+    assert_same("s_col", bits(s_col[:, bb]), esc)
+    assert_same("dequant col", bits(y_col[:, bi]), oracle.mx_dequantize(ec, esc))
+    del q_row, s_row, q_col, s_col, y_col
     torch.cuda.empty_cache()
