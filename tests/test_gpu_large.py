@@ -1,13 +1,14 @@
 """GPU parity on a tensor past 2^31 elements: 1081349 x 2048 BF16 (4.4 GB), quantized to
 per-token NVFP4, to rowwise and to both MXFP8 copies at full size on the GPU and dequantized
 again, and scattered as tokens to routed rows, then compared with the oracle on sampled rows
-(and sampled 32-row blocks of the columnwise copy).  Both formats are row-local (page "Towards
-Blackwell-native 8-bit and 4-bit RL", sections "Format background" and "Per-token activation
-scaling": a row's codes and scales depend on that row only), so the oracle's result on a
-subset of the rows is that subset of its result on the whole tensor.  The sampled rows lie
-at the start, on both sides of element 2^31 (row 2^20), at seeded random places and in the
-last rows; element and byte offsets there need more than 31 bits.  Outputs carry guard
-bytes on both sides, checked on the device."""
+(and sampled 32-row blocks of the columnwise copy).  Per-token NVFP4 and rowwise MXFP8 are
+row-local (page "Towards Blackwell-native 8-bit and 4-bit RL", sections "Format background"
+and "Per-token activation scaling": a row's codes and scales depend on that row only), so
+the oracle's result on a subset of the rows is that subset of its result on the whole
+tensor; a columnwise block depends on its 32 rows only.  The sampled rows lie at the start,
+on both sides of element 2^31 (row 2^20), at seeded random places and in the last rows;
+element and byte offsets there need more than 31 bits.  The per-token and rowwise outputs
+carry guard bytes on both sides, checked on the device."""
 import numpy as np
 import pytest
 import torch
