@@ -155,3 +155,35 @@ def test_mx_both_past_2_pow_31_elements(big):
     assert_same("dequant col", bits(y_col[:, bi]), oracle.mx_dequantize(ec, esc))
     del q_row, s_row, q_col, s_col, y_col
     torch.cuda.empty_cache()
+
+
+def test_nv_dequant_split_into_several_launches():
+    """The NVFP4 dequantizers index half blocks (8 elements) with 32 bits, so a tensor of 2^31
+    half blocks or more is dequantized in row ranges, one launch each: at K = 2048 a launch
+    takes 2^23 rows.  R = 2^23 + 1000 rows of random codes, block scales (NaN codes included)
+    and token scales (34 GB of BF16 output) cross that boundary; the per-token dequant and the
+    per-group one (three groups, the middle one spanning the boundary) are compared with the
+    oracle's dequant on sampled rows (the per-group one is the per-token formula with each
+    row's group scale)."""
+    Rb = (1 << 23) + 1000
+    log("nv dequant %dx%d in several launches" % (Rb, K))
+    g = torch.Generator(device="cuda").manual_seed(47)
+    q = torch.randint(0, 256, (Rb, K // 2), generator=g, dtype=torch.uint8, device="cuda")
+    sb = torch.randint(0, 256, (Rb, K // 16), generator=g, dtype=torch.uint8, device="cuda")
+    st = torch.exp2(torch.randint(-30, 30, (Rb,), generator=g, device="cuda").float()) * \
+        torch.rand(Rb, generator=g, device="cuda")
+    rows = np.unique(np.concatenate([np.arange(3), np.arange((1 << 23) - 3, (1 << 23) + 3),
+                                     np.random.default_rng(53).integers(0, Rb, 16), np.arange(Rb - 3, Rb)]))
+    ri = torch.from_numpy(rows).cuda()
+    qh, sbh, sth = bits(q[ri]), bits(sb[ri]), bits(st[ri]).view(np.float32)
+    y = bsq.nv_dequantize(q, sb, st)
+    torch.cuda.synchronize()
+    assert_same("per-token dequant", bits(y[ri]), oracle.nv_dequantize(qh, sbh, sth))
+    off = np.array([0, 1000, (1 << 23) + 500, Rb], np.int64)
+    s_group = torch.tensor([0.75, 3.0e-3, 1.5e4], dtype=torch.float32, device="cuda")
+    bsq.nv_dequantize_per_group(q, sb, s_group, torch.from_numpy(off).cuda(), y=y)
+    torch.cuda.synchronize()
+    st_rows = s_group.cpu().numpy()[np.searchsorted(off, rows, side="right") - 1]
+    assert_same("per-group dequant", bits(y[ri]), oracle.nv_dequantize(qh, sbh, st_rows))
+    del q, sb, st, y
+    torch.cuda.empty_cache()
