@@ -187,3 +187,32 @@ def test_nv_dequant_split_into_several_launches():
     assert_same("per-group dequant", bits(y[ri]), oracle.nv_dequantize(qh, sbh, st_rows))
     del q, sb, st, y
     torch.cuda.empty_cache()
+
+
+def test_nv_dequant_2d_split_into_several_launches():
+    """The same split for the 16x16-tile dequant, whose row ranges are whole tiles: R = 2^23 +
+    1008 rows of random codes, random tile scales and three groups (offsets multiples of 16,
+    the middle group spanning the boundary at row 2^23).  Sampled 16-row tiles are compared
+    with the oracle's 2-D dequant of those tiles alone, each as a group of its own with its
+    group's scale (an element depends only on its code, its tile's scale and its group's
+    scale)."""
+    Rb = (1 << 23) + 1008
+    log("nv dequant 2d %dx%d in several launches" % (Rb, K))
+    g = torch.Generator(device="cuda").manual_seed(59)
+    q = torch.randint(0, 256, (Rb, K // 2), generator=g, dtype=torch.uint8, device="cuda")
+    sb = torch.randint(0, 256, (Rb // 16, K // 16), generator=g, dtype=torch.uint8, device="cuda")
+    off = np.array([0, 1008, (1 << 23) + 496, Rb], np.int64)
+    s_group = torch.tensor([2.5, 6.0e-5, 7.0e3], dtype=torch.float32, device="cuda")
+    y = bsq.nv_dequantize_2d(q, sb, s_group, torch.from_numpy(off).cuda())
+    torch.cuda.synchronize()
+    nt = Rb // 16
+    tiles = np.unique(np.concatenate([[0, 1, (1 << 19) - 1, 1 << 19, (1 << 19) + 1, nt - 1],
+                                      np.random.default_rng(61).integers(0, nt, 8)]))
+    rows = (16 * tiles[:, None] + np.arange(16)[None, :]).reshape(-1)
+    ri, ti = torch.from_numpy(rows).cuda(), torch.from_numpy(tiles).cuda()
+    sg = s_group.cpu().numpy()[np.searchsorted(off, 16 * tiles, side="right") - 1]
+    want = oracle.nv_dequantize_2d(bits(q[ri]), bits(sb[ti]), sg.astype(np.float32),
+                                   np.arange(0, 16 * tiles.size + 1, 16, dtype=np.int64))
+    assert_same("2-D dequant", bits(y[ri]), want)
+    del q, sb, y
+    torch.cuda.empty_cache()
