@@ -1,7 +1,8 @@
 """GPU parity on a tensor past 2^31 elements: 1081349 x 2048 BF16 (4.4 GB), quantized to
 per-token NVFP4, to rowwise and to both MXFP8 copies at full size on the GPU and dequantized
-again, and scattered as tokens to routed rows, then compared with the oracle on sampled rows
-(and sampled 32-row blocks of the columnwise copy).  Per-token NVFP4 and rowwise MXFP8 are
+again, scattered as tokens to routed rows, and quantized with one scale per row group, then
+compared with the oracle on sampled rows (and sampled 32-row blocks of the columnwise copy);
+and the NVFP4 dequantizers on tensors large enough to be split into several launches.  Per-token NVFP4 and rowwise MXFP8 are
 row-local (page "Towards Blackwell-native 8-bit and 4-bit RL", sections "Format background"
 and "Per-token activation scaling": a row's codes and scales depend on that row only), so
 the oracle's result on a subset of the rows is that subset of its result on the whole
@@ -156,6 +157,36 @@ def test_mx_both_past_2_pow_31_elements(big):
     del q_row, s_row, q_col, s_col, y_col
     torch.cuda.empty_cache()
 
+
+def test_nv_per_group_past_2_pow_31_elements(big):
+    """Standard NVFP4 with one FP32 scale per row group (page "Towards Blackwell-native 8-bit
+    and 4-bit RL", section "Format background": the coarse FP32 scale's scope is a recipe
+    choice) on the whole tensor in three groups, the last one starting past element 2^31.
+    A row's bytes depend on its own values and its group's maximum only, so for each group
+    the oracle runs on that group's sampled rows plus one row that holds the group's largest
+    magnitude (located with torch on the GPU), as a group of its own: its scale is the
+    group's, and the sampled rows' bytes must equal the GPU's."""
+    x, _ = big
+    off = np.array([0, 500000, (1 << 20) + 7, R], np.int64)
+    log("nv per-group %dx%d, %d groups" % (R, K, off.size - 1))
+    q, sb, s_group, status = bsq.nv_quantize_nvfp4_per_group(x, torch.from_numpy(off).cuda())
+    torch.cuda.synchronize()
+    assert int(status.item()) == bsq.BSQ_OK
+    sg = bits(s_group)
+    for g in range(off.size - 1):
+        a, b = int(off[g]), int(off[g + 1])
+        rows = ROWS[(ROWS >= a) & (ROWS < b)]
+        assert rows.size > 0
+        top = a + int(torch.argmax(x[a:b].abs().amax(dim=1).float()).item())   # row of the group maximum
+        sub = np.concatenate([rows, [top]])
+        eq, esb, es, ok = oracle.nv_quantize_per_group(bits(x[torch.from_numpy(sub).cuda()]), [0, sub.size])
+        assert ok
+        assert_same("s_group[%d]" % g, sg[g:g + 1], es.view(np.uint32))
+        ri = torch.from_numpy(rows).cuda()
+        assert_same("sb group %d" % g, bits(sb[ri]), esb[:-1])
+        assert_same("q group %d" % g, bits(q[ri]), eq[:-1])
+    del q, sb, s_group
+    torch.cuda.empty_cache()
 
 def test_nv_dequant_split_into_several_launches():
     """The NVFP4 dequantizers index half blocks (8 elements) with 32 bits, so a tensor of 2^31
