@@ -1,6 +1,7 @@
 """GPU parity on a tensor past 2^31 elements: 1081349 x 2048 BF16 (4.4 GB), quantized to
 per-token NVFP4, to rowwise and to both MXFP8 copies at full size on the GPU and dequantized
-again, scattered as tokens to routed rows, and quantized with one scale per row group, then
+again, scattered as tokens to routed rows, and quantized with one scale per row group (1x16
+and 16x16 blocks), then
 compared with the oracle on sampled rows (and sampled 32-row blocks of the columnwise copy);
 and the NVFP4 dequantizers on tensors large enough to be split into several launches.  Per-token NVFP4 and rowwise MXFP8 are
 row-local (page "Towards Blackwell-native 8-bit and 4-bit RL", sections "Format background"
@@ -185,6 +186,38 @@ def test_nv_per_group_past_2_pow_31_elements(big):
         ri = torch.from_numpy(rows).cuda()
         assert_same("sb group %d" % g, bits(sb[ri]), esb[:-1])
         assert_same("q group %d" % g, bits(q[ri]), eq[:-1])
+    del q, sb, s_group
+    torch.cuda.empty_cache()
+
+def test_nv_2d_past_2_pow_31_elements(big):
+    """NVFP4 with 16x16 tiles under one scale per row group (page "NVIDIA verified the 4-bit
+    NVFP4 format on a Mamba-Transformer (12B) at 10 trillion tokens": 2-D block scaling of the
+    weights) on the first 2^20 + 2^15 rows in three groups of whole tiles, the last starting
+    past element 2^31.  A tile's bytes depend on its own values and its group's maximum only,
+    so for each group the oracle runs on that group's sampled tiles plus the tile that holds
+    the group's largest magnitude, as a group of its own."""
+    x, _ = big
+    R16 = R - R % 16
+    off = np.array([0, 499984, (1 << 20) + 16, R16], np.int64)
+    log("nv 16x16 tiles %dx%d, %d groups" % (R16, K, off.size - 1))
+    xm = x[:R16]
+    q, sb, s_group, status = bsq.nv_quantize_nvfp4_2d(xm, torch.from_numpy(off).cuda())
+    torch.cuda.synchronize()
+    assert int(status.item()) == bsq.BSQ_OK
+    sg = bits(s_group)
+    for g in range(off.size - 1):
+        a, b = int(off[g]), int(off[g + 1])
+        tiles = np.unique(ROWS[(ROWS >= a) & (ROWS < b)] // 16)
+        assert tiles.size > 0
+        top = a + int(torch.argmax(xm[a:b].abs().amax(dim=1).float()).item())
+        sub_tiles = np.concatenate([tiles, [top // 16]])
+        rows = (16 * sub_tiles[:, None] + np.arange(16)[None, :]).reshape(-1)
+        eq, esb, es, ok = oracle.nv_quantize_2d(bits(xm[torch.from_numpy(rows).cuda()]), [0, rows.size])
+        assert ok
+        assert_same("s_group[%d]" % g, sg[g:g + 1], es.view(np.uint32))
+        n = 16 * tiles.size
+        assert_same("sb group %d" % g, bits(sb[torch.from_numpy(tiles).cuda()]), esb[:-1])
+        assert_same("q group %d" % g, bits(q[torch.from_numpy(rows[:n]).cuda()]), eq[:n])
     del q, sb, s_group
     torch.cuda.empty_cache()
 
