@@ -77,7 +77,16 @@ def test_nv_per_token_past_2_pow_31_elements(big):
     assert_same("sb", _rows(sb), esb)
     assert_same("q", _rows(q), eq)
     assert_same("dequant", _rows(y), oracle.nv_dequantize(eq, esb, est))
-    del q, sb, st, qb, sbb, stb, y
+    del y
+    # grouped by expert: the same bytes as the flat call (row-local), offsets checked on the device
+    off = torch.tensor([0, 7, (1 << 20) + 1, (1 << 20) + 1, R], dtype=torch.int64, device="cuda")
+    q2, sb2, st2 = torch.empty_like(q), torch.empty_like(sb), torch.empty_like(st)
+    status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    bsq.nv_quantize_nvfp4_per_token_grouped(x, off, q2, sb2, st2, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == bsq.BSQ_OK
+    assert torch.equal(q2, q) and torch.equal(sb2, sb) and torch.equal(st2.view(torch.int32), st.view(torch.int32))
+    del q, sb, st, qb, sbb, stb, q2, sb2, st2
     torch.cuda.empty_cache()
 
 
