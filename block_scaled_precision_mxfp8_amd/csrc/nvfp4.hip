@@ -240,6 +240,28 @@ __device__ __forceinline__ void quant_span(const uint4 (&v)[NS], int64_t r0, int
     }
 }
 
+// Row of one-wave workgroup b out of n when the rows are dealt to the XCDs in chunks of
+// NV_XCD_CHUNK consecutive rows.  Workgroups go to the eight XCDs in turn (b % 8), so
+// workgroup b takes row (8 (c / CH) + b % 8) CH + c % CH with c = b / 8: each XCD walks
+// contiguous chunks of the tensor.  The rows past the last whole round of 8 chunks keep
+// row = b, so the map is a bijection of [0, n).  Measured on the per-token quantizer with the
+// following read (one box, interleaved): 524288 x 2048 442.1 -> 434.1 us, the layer step
+// 1111.6 -> 1103.8 us; 262144 x 4096 459.7 -> 448.9 us, 196608 x 2048 165.0 -> 163.4 us;
+// with the rows starting 37 or 300 rows into an allocation, 440.0 -> 436.8 and 442.7 ->
+// 442.0 us.  Other chunk sizes were not monotone: 64 / 128 / 256 / 1024 rows took 447.3 /
+// 435.3 / 440.5 / 444.2 us on 524288 x 2048 (the memory-only pattern behaves alike), and 128
+// lost on 262144 x 4096.  The quantize-then-scatter (one token per workgroup, writes
+// scattered by the routing) became 4% slower with it, and the dequantizer's pattern too;
+// they keep b.
+constexpr int64_t NV_XCD_CHUNK = 512;
+__device__ __forceinline__ int64_t xcd_chunk_row(int64_t b, int64_t n) {
+    constexpr int64_t CH = NV_XCD_CHUNK;
+    const int64_t full = n / (8 * CH) * (8 * CH);
+    if (b >= full) return b;
+    const int64_t c = b >> 3;
+    return ((c / CH) * 8 + (b & 7)) * CH + c % CH;
+}
+
 // One span per wave, WAVES waves per workgroup, per-token scales.
 template <int NS, int RPW, bool FULL, int WAVES>
 __global__ __launch_bounds__(64 * WAVES)
@@ -251,7 +273,8 @@ void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
     const int wave = wave_id();
     const int lane = threadIdx.x & 63;
     if (status != nullptr && blockIdx.x == 0 && wave == 0) check_offsets(offsets, E, R, status);
-    const int64_t r0 = ((int64_t)blockIdx.x * WAVES + wave) * RPW;
+    const int64_t r0 = WAVES == 1 && RPW == 1 ? xcd_chunk_row(blockIdx.x, gridDim.x)
+                                               : ((int64_t)blockIdx.x * WAVES + wave) * RPW;
     if (r0 >= R) return;
     __shared__ __align__(16) uint8_t lds_sb[WAVES][32 * NS];
     const int cpr = (int)(K >> 3);                    // 8-element chunks per row
@@ -830,8 +853,10 @@ void nv_dequant_kernel(const uint32_t* __restrict__ q, const uint8_t* __restrict
 // 444.5-445 us on the 524288 x 2048 routed rows inside the step (the step 6172-6186 ->
 // 6210-6219 GB/s), 168.7 -> 166.3 us on 196608 x 2048 timed with the following read; the
 // same change made two-row spans slower (262144 x 768: 82.3 -> 88.7 us), which keep
-// NV_WAVES.  Either way the grid has one wave per span, so nv_quant_launch_fits (which
-// counts NV_WAVES-wave workgroups, the stricter count) covers both.
+// NV_WAVES.  The one-wave workgroups take their rows in XCD chunks (xcd_chunk_row, which
+// needs the grid to be exactly one workgroup per row).  Either way the grid has one wave per
+// span, so nv_quant_launch_fits (which counts NV_WAVES-wave workgroups, the stricter count)
+// covers both.
 template <int NS, int RPW>
 static void launch_rows(const void* x, int64_t R, int64_t K, void* q, void* sb, float* st,
                         const int64_t* off, int64_t E, int32_t* status, hipStream_t stream) {

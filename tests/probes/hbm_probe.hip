@@ -44,8 +44,19 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ x, 
     st<NT>(y + i, ld_nt(x + i));
 }
 
+// Row of workgroup b of n when rows are dealt to the eight XCDs (b % 8) in chunks of 512
+// consecutive rows, as the per-token quantizer deals them; rows past the last whole round of
+// eight chunks keep row = b.
+__device__ __forceinline__ int64_t chunk_row(int64_t b, int64_t n) {
+    const int64_t full = n / 4096 * 4096;
+    if (b >= full) return b;
+    const int64_t c = b >> 3;
+    return ((c / 512) * 8 + (b & 7)) * 512 + c % 512;
+}
+
 // The per-token NVFP4 quantizer's traffic on rows of 2048 BF16 (256 pieces): one wave per
-// row and per workgroup, four 16-byte loads a lane at raised wave priority, then per row
+// row and per workgroup, the rows dealt to the XCDs as the quantizer deals them (chunk_row),
+// four 16-byte loads a lane at raised wave priority, then per row
 // 1 KiB of codes as 4-byte stores (256 bytes per store instruction), 128 scale bytes gathered
 // in LDS and written as eight 16-byte stores, and one 4-byte token scale.  The stored values
 // are XORs of the loaded ones, not codes.
@@ -53,7 +64,7 @@ __global__ __launch_bounds__(64) void nv_pattern_kernel(const u32x4* __restrict_
                                                         uint8_t* __restrict__ sb, float* __restrict__ s) {
     __shared__ __align__(16) uint8_t lsb[1][128];
     const int lane = threadIdx.x & 63, wave = 0;
-    const int64_t row = (int64_t)blockIdx.x;
+    const int64_t row = chunk_row(blockIdx.x, gridDim.x);
     const u32x4* xr = x + row * 256;
     u32x4 v[4];
     __builtin_amdgcn_s_setprio(3);

@@ -54,10 +54,10 @@ def test_copy_write_and_read_probes():
 
 
 def test_nv_pattern_probe_writes_the_quantizers_bytes():
-    log("hbm probe NVFP4 pattern, 64 rows")
+    log("hbm probe NVFP4 pattern, 8256 rows")
     hp = _lib()
     s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    R, K, pad = 64, 2048, 4096
+    R, K, pad = 8256, 2048, 4096                   # two rounds of 512-row chunks on 8 XCDs, and 64 more
     x = torch.randint(0, 0x7F80, (R * K,), dtype=torch.int32, device="cuda").to(torch.int16)
     q = torch.full((R * K // 2 + 2 * pad,), 0xA5, dtype=torch.uint8, device="cuda")
     sb = torch.full((R * K // 16 + 2 * pad,), 0xA5, dtype=torch.uint8, device="cuda")
