@@ -849,12 +849,12 @@ void nv_dequant_kernel(const uint32_t* __restrict__ q, const uint8_t* __restrict
 
 // Spans of RPW rows per wave; FULL when every span fills its NS slots exactly (the last
 // span of an odd row count under RPW = 2 takes the bounds-checked kernel).  One-row spans
-// run one wave per workgroup, so that consecutive rows go to different XCDs: 450-451 ->
-// 444.5-445 us on the 524288 x 2048 routed rows inside the step (the step 6172-6186 ->
-// 6210-6219 GB/s), 168.7 -> 166.3 us on 196608 x 2048 timed with the following read; the
+// run one wave per workgroup: 450-451 -> 444.5-445 us on the 524288 x 2048 routed rows
+// inside the step (the step 6172-6186 -> 6210-6219 GB/s), 168.7 -> 166.3 us on 196608 x
+// 2048 timed with the following read, then with consecutive rows on different XCDs; the
 // same change made two-row spans slower (262144 x 768: 82.3 -> 88.7 us), which keep
-// NV_WAVES.  The one-wave workgroups take their rows in XCD chunks (xcd_chunk_row, which
-// needs the grid to be exactly one workgroup per row).  Either way the grid has one wave per
+// NV_WAVES.  The one-wave workgroups now take their rows in XCD chunks (xcd_chunk_row,
+// which needs the grid to be exactly one workgroup per row).  Either way the grid has one wave per
 // span, so nv_quant_launch_fits (which counts NV_WAVES-wave workgroups, the stricter count)
 // covers both.
 template <int NS, int RPW>
