@@ -240,22 +240,23 @@ __device__ __forceinline__ void quant_span(const uint4 (&v)[NS], int64_t r0, int
     }
 }
 
-// Row of one-wave workgroup b out of n when the rows are dealt to the XCDs in chunks of
-// NV_XCD_CHUNK consecutive rows.  Workgroups go to the eight XCDs in turn (b % 8), so
-// workgroup b takes row (8 (c / CH) + b % 8) CH + c % CH with c = b / 8: each XCD walks
-// contiguous chunks of the tensor.  The rows past the last whole round of 8 chunks keep
-// row = b, so the map is a bijection of [0, n).  Measured on the per-token quantizer with the
-// following read (one box, interleaved): 524288 x 2048 442.1 -> 434.1 us, the layer step
-// 1111.6 -> 1103.8 us; 262144 x 4096 459.7 -> 448.9 us, 196608 x 2048 165.0 -> 163.4 us;
-// with the rows starting 37 or 300 rows into an allocation, 440.0 -> 436.8 and 442.7 ->
-// 442.0 us.  Other chunk sizes were not monotone: 64 / 128 / 256 / 1024 rows took 447.3 /
-// 435.3 / 440.5 / 444.2 us on 524288 x 2048 (the memory-only pattern behaves alike), and 128
-// lost on 262144 x 4096.  The quantize-then-scatter (one token per workgroup, writes
-// scattered by the routing) became 4% slower with it, and the dequantizer's pattern too;
-// they keep b.
-constexpr int64_t NV_XCD_CHUNK = 512;
-__device__ __forceinline__ int64_t xcd_chunk_row(int64_t b, int64_t n) {
-    constexpr int64_t CH = NV_XCD_CHUNK;
+// Workgroup index that workgroup b of n takes when the rows are dealt to the XCDs in chunks
+// of NV_XCD_CHUNK_ROWS consecutive rows (CH workgroups).  Workgroups go to the eight XCDs
+// in turn (b % 8), so workgroup b takes index (8 (c / CH) + b % 8) CH + c % CH with c = b /
+// 8: each XCD walks contiguous chunks of the tensor.  The workgroups past the last whole
+// round of 8 chunks keep index b, so the map is a bijection of [0, n).  Measured on the
+// per-token quantizer with the following read (one box, interleaved): one-row spans,
+// 524288 x 2048 442.1 -> 434.1 us (the layer step 1111.6 -> 1103.8 us), 262144 x 4096 459.7
+// -> 448.9, 196608 x 2048 165.0 -> 163.4, and with the rows starting 37 or 300 rows into an
+// allocation 440.0 -> 436.8 and 442.7 -> 442.0; two-row spans, 262144 x 768 80.9 -> 79.9,
+// 524288 x 512 104.2 -> 102.7, 1048576 x 256 151.4 -> 146.2.  Other chunk sizes were not
+// monotone: 64 / 128 / 256 / 1024 rows took 447.3 / 435.3 / 440.5 / 444.2 us on 524288 x
+// 2048 (the memory-only pattern behaves alike), and 128 lost on 262144 x 4096.  The
+// quantize-then-scatter (one token per workgroup, writes scattered by the routing) became
+// 4% slower with it, and the dequantizer's pattern too; they keep b.
+constexpr int64_t NV_XCD_CHUNK_ROWS = 512;
+template <int64_t CH>
+__device__ __forceinline__ int64_t xcd_chunk(int64_t b, int64_t n) {
     const int64_t full = n / (8 * CH) * (8 * CH);
     if (b >= full) return b;
     const int64_t c = b >> 3;
@@ -273,8 +274,8 @@ void nv_quant_rows_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ q,
     const int wave = wave_id();
     const int lane = threadIdx.x & 63;
     if (status != nullptr && blockIdx.x == 0 && wave == 0) check_offsets(offsets, E, R, status);
-    const int64_t r0 = WAVES == 1 && RPW == 1 ? xcd_chunk_row(blockIdx.x, gridDim.x)
-                                               : ((int64_t)blockIdx.x * WAVES + wave) * RPW;
+    const int64_t wg = xcd_chunk<NV_XCD_CHUNK_ROWS / (WAVES * RPW)>(blockIdx.x, gridDim.x);
+    const int64_t r0 = (wg * WAVES + wave) * RPW;
     if (r0 >= R) return;
     __shared__ __align__(16) uint8_t lds_sb[WAVES][32 * NS];
     const int cpr = (int)(K >> 3);                    // 8-element chunks per row
@@ -853,8 +854,8 @@ void nv_dequant_kernel(const uint32_t* __restrict__ q, const uint8_t* __restrict
 // inside the step (the step 6172-6186 -> 6210-6219 GB/s), 168.7 -> 166.3 us on 196608 x
 // 2048 timed with the following read, then with consecutive rows on different XCDs; the
 // same change made two-row spans slower (262144 x 768: 82.3 -> 88.7 us), which keep
-// NV_WAVES.  The one-wave workgroups now take their rows in XCD chunks (xcd_chunk_row,
-// which needs the grid to be exactly one workgroup per row).  Either way the grid has one wave per
+// NV_WAVES.  Both now take their rows in XCD chunks of 512 rows (xcd_chunk, which needs the
+// grid to be exactly one workgroup per WAVES spans, as here).  Either way the grid has one wave per
 // span, so nv_quant_launch_fits (which counts NV_WAVES-wave workgroups, the stricter count)
 // covers both.
 template <int NS, int RPW>

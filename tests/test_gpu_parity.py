@@ -153,7 +153,8 @@ def test_mx_dequant_round_trip_matches_oracle(M, K):
 # with K = 256, 512, 768 fill whole register slots
 NV_SHAPES = [(1, 16), (5, 32), (3, 48), (8, 64), (6, 256), (9, 512), (10, 512), (17, 768),
              (16, 768), (2, 768), (4, 1040), (33, 2048), (2, 4096), (3, 4112), (2, 8208),
-             (4096, 1040), (8229, 1040)]   # one-row spans dealt to the XCDs in 512-row chunks, and a tail
+             (4096, 1040), (8229, 1040),   # one-row spans dealt to the XCDs in 512-row chunks, and a tail
+             (4096, 512), (8197, 768)]     # two-row spans, the same chunks, a tail and an odd last row
 
 
 @pytest.mark.parametrize("R,K", NV_SHAPES)
